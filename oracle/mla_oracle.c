@@ -1,0 +1,232 @@
+/*
+ * Plain fp64 CPU oracle for split-KV MLA decode attention over a paged FP8 cache.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call this
+ * file; only the test suite, the smoke check and the benchmark's CPU-baseline leg use
+ * it. It shares no code, header, table or constant generator with the HIP library.
+ *
+ * What it computes is the plain, unsplit definition of attention decode that the
+ * split-KV method reaches faster:
+ *
+ *   Geometry [TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA decode slower after #19338",
+ *   Setup]: each cached token is one row of 576 FP8 E4M3 bytes, a 512-wide latent
+ *   followed by a 64-wide rope part; the cache is paged with 32 tokens per page; q and
+ *   KV are both E4M3. V is the 512-wide latent of the same row (MLA absorption: the
+ *   latent serves as both the K prefix and V).
+ *
+ *   Scales [same issue, Repro 1: the run() arguments softmax_scale and output_scale]:
+ *   scores are softmax_scale * (q . k); output_scale multiplies O only.
+ *
+ *   Causal MTP verify [the q = 8 "MTP verify" shape of the same issue's Setup]: with
+ *   q_len query tokens per request, query token j sees KV tokens 0 .. L - q_len + j
+ *   inclusive, i.e. n_j = L - q_len + j + 1 of them; q_len = 1 gives n = L.
+ *
+ *   For each request b, query j, head h:
+ *     s_i  = softmax_scale * sum_{d<576} q_d * K_{i,d}            (fp64, exact sum)
+ *     m    = max_i s_i,  w_i = exp(s_i - m),  l = sum_i w_i
+ *     O_d  = output_scale * sum_i w_i * V_{i,d} / l                (d < 512)
+ *     LSE  = m + ln(l)        (natural log of sum_i exp(s_i); output_scale excluded)
+ *
+ * The (max, sum, O) triple is the per-row state the reduction merges [TensorRT-LLM PR
+ * #20380 "trtllm-gen FMHA: split the KV partials of a row across thread groups in
+ * fmhaReductionKernel", Description]; here it is formed once over all keys, unsplit.
+ *
+ * E4M3 decoding follows the OCP FP8 E4M3 ("fn") encoding: 1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals m * 2^-9, the codes 0x7F / 0xFF are NaN and
+ * there is no infinity. Every E4M3 value is exact in fp64 (and in BF16, as PR #17441
+ * "m3 decode perf clean" notes for the widening of E4M3 to BF16).
+ *
+ * Exactness of the dot product: every E4M3 product is a multiple of 2^-18 with
+ * magnitude below 2^18, so every partial sum of at most 576 of them is a multiple of
+ * 2^-18 below 2^28 and fits fp64's 53-bit significand; the sum is exact in any order.
+ *
+ * Row order: flat row id r = (b * q_len + j) * H + h, the layout of q [B][q_len][H][576]
+ * and of O [B][q_len][H][512].
+ *
+ * Threads: rows are handed out to POSIX threads through an atomic counter; each row's
+ * arithmetic is sequential and independent of the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_D_QK 576
+#define ORACLE_D_V 512
+#define ORACLE_PAGE 32
+
+/* Decode one OCP E4M3FN code to fp64. */
+double oracle_e4m3_to_double(uint8_t code) {
+  int sign = code >> 7;
+  int expo = (code >> 3) & 15;
+  int mant = code & 7;
+  double v;
+  if (expo == 15 && mant == 7) return NAN;
+  if (expo == 0)
+    v = ldexp((double)mant, -9); /* 0.mmm * 2^(1-7) */
+  else
+    v = ldexp(8.0 + mant, expo - 7 - 3); /* 1.mmm * 2^(e-7) */
+  return sign ? -v : v;
+}
+
+int oracle_hw_threads(void) {
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+typedef struct {
+  const uint8_t* q;
+  const uint8_t* kv;
+  const int32_t* bt;
+  const int32_t* kv_lens;
+  int32_t batch, q_len, heads;
+  int64_t bt_stride, num_pages;
+  double softmax_scale, output_scale;
+  const int64_t* rows;
+  int64_t nrows;
+  double* out_o;
+  double* out_lse;
+  double table[256];
+  int64_t next; /* atomic row counter */
+  int error;    /* first error seen (atomic) */
+} oracle_job;
+
+/* Error codes (negative). */
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_PAGE (-2)
+#define ORACLE_ERR_ROW (-3)
+#define ORACLE_ERR_NOMEM (-4)
+
+static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
+  int64_t r = J->rows ? J->rows[idx] : idx;
+  int64_t rows_total = (int64_t)J->batch * J->q_len * J->heads;
+  if (r < 0 || r >= rows_total) return ORACLE_ERR_ROW;
+  int64_t bj = r / J->heads;
+  int32_t b = (int32_t)(bj / J->q_len);
+  int32_t j = (int32_t)(bj % J->q_len);
+  int64_t L = J->kv_lens[b];
+  int64_t n = L - J->q_len + j + 1; /* keys visible to query token j */
+  if (n < 1) return ORACLE_ERR_ARG;
+  if ((n + ORACLE_PAGE - 1) / ORACLE_PAGE > J->bt_stride) return ORACLE_ERR_ARG;
+
+  double qd[ORACLE_D_QK];
+  const uint8_t* qrow = J->q + r * ORACLE_D_QK;
+  for (int d = 0; d < ORACLE_D_QK; ++d) qd[d] = J->table[qrow[d]];
+
+  /* scores s_i = softmax_scale * (q . K_i) */
+  double m = -INFINITY;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
+    if (page < 0 || page >= J->num_pages) return ORACLE_ERR_PAGE;
+    const uint8_t* k = J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;
+    double dot = 0.0;
+    for (int d = 0; d < ORACLE_D_QK; ++d) dot += qd[d] * J->table[k[d]];
+    s[i] = J->softmax_scale * dot;
+    if (s[i] > m) m = s[i];
+  }
+  /* weights, normaliser, and the weighted sum of V (the first 512 bytes of each row) */
+  for (int d = 0; d < ORACLE_D_V; ++d) acc[d] = 0.0;
+  double l = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
+    const uint8_t* v = J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;
+    double w = exp(s[i] - m);
+    l += w;
+    for (int d = 0; d < ORACLE_D_V; ++d) acc[d] += w * J->table[v[d]];
+  }
+  double* o = J->out_o + idx * ORACLE_D_V;
+  for (int d = 0; d < ORACLE_D_V; ++d) o[d] = J->output_scale * acc[d] / l;
+  J->out_lse[idx] = m + log(l);
+  return 0;
+}
+
+static void* worker(void* arg) {
+  oracle_job* J = (oracle_job*)arg;
+  int64_t cap = 0;
+  double* s = NULL;
+  double acc[ORACLE_D_V];
+  for (;;) {
+    int64_t idx = __atomic_fetch_add(&J->next, 1, __ATOMIC_RELAXED);
+    if (idx >= J->nrows) break;
+    if (__atomic_load_n(&J->error, __ATOMIC_RELAXED) != 0) break;
+    int64_t r = J->rows ? J->rows[idx] : idx;
+    int64_t need = 1;
+    if (r >= 0 && r < (int64_t)J->batch * J->q_len * J->heads) {
+      int32_t b = (int32_t)(r / J->heads / J->q_len);
+      need = J->kv_lens[b] > 0 ? J->kv_lens[b] : 1;
+    }
+    if (need > cap) {
+      free(s);
+      s = (double*)malloc(sizeof(double) * (size_t)need);
+      cap = need;
+      if (!s) {
+        int zero = 0;
+        __atomic_compare_exchange_n(&J->error, &zero, ORACLE_ERR_NOMEM, 0, __ATOMIC_RELAXED,
+                                    __ATOMIC_RELAXED);
+        break;
+      }
+    }
+    int rc = one_row(J, idx, s, acc);
+    if (rc != 0) {
+      int zero = 0;
+      __atomic_compare_exchange_n(&J->error, &zero, rc, 0, __ATOMIC_RELAXED, __ATOMIC_RELAXED);
+      break;
+    }
+  }
+  free(s);
+  return NULL;
+}
+
+/*
+ * Compute O (fp64 [nrows][512]) and LSE (fp64 [nrows]) for the listed flat rows
+ * (rows == NULL: all B*q_len*H rows in order). Inputs are host arrays:
+ *   q       uint8 E4M3 [B][q_len][H][576]
+ *   kv      uint8 E4M3 [num_pages][32][576]
+ *   bt      int32 [B][bt_stride], page indices into kv
+ *   kv_lens int32 [B], each >= q_len
+ * nthreads <= 0 uses every online core. Returns 0 or a negative error code; on error
+ * the outputs are unspecified.
+ */
+int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
+                           const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                           int32_t num_heads, int64_t bt_stride, int64_t num_pages,
+                           double softmax_scale, double output_scale, const int64_t* rows,
+                           int64_t nrows, double* out_o, double* out_lse, int nthreads) {
+  if (!q || !kv || !bt || !kv_lens || !out_o || !out_lse) return ORACLE_ERR_ARG;
+  if (batch < 1 || q_len < 1 || num_heads < 1 || bt_stride < 1 || num_pages < 1 || nrows < 0)
+    return ORACLE_ERR_ARG;
+  oracle_job* J = (oracle_job*)calloc(1, sizeof(oracle_job));
+  if (!J) return ORACLE_ERR_NOMEM;
+  J->q = q;
+  J->kv = kv;
+  J->bt = bt;
+  J->kv_lens = kv_lens;
+  J->batch = batch;
+  J->q_len = q_len;
+  J->heads = num_heads;
+  J->bt_stride = bt_stride;
+  J->num_pages = num_pages;
+  J->softmax_scale = softmax_scale;
+  J->output_scale = output_scale;
+  J->rows = rows;
+  J->nrows = nrows;
+  J->out_o = out_o;
+  J->out_lse = out_lse;
+  for (int c = 0; c < 256; ++c) J->table[c] = oracle_e4m3_to_double((uint8_t)c);
+
+  int nt = nthreads > 0 ? nthreads : oracle_hw_threads();
+  if (nt > nrows) nt = nrows > 0 ? (int)nrows : 1;
+  if (nt > 256) nt = 256;
+  pthread_t tid[256];
+  int started = 0;
+  for (int t = 1; t < nt; ++t) {
+    if (pthread_create(&tid[started], NULL, worker, J) == 0) ++started;
+  }
+  worker(J);
+  for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+  int rc = J->error;
+  free(J);
+  return rc;
+}

@@ -1,0 +1,225 @@
+"""Checks that pin the fp64 oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes ``lib_path`` (None = the real oracle) and raises
+AssertionError when the oracle disagrees with:
+  * torch's own float8_e4m3fn decoding (a separate library routine);
+  * exact rational arithmetic (``fractions.Fraction``) for the score of a single key;
+  * closed forms: one key gives O = V, equal scores give the mean of V and LSE = ln n;
+  * 50-digit brute force (mpmath) with no max subtraction, on tiny inputs;
+  * torch's fp64 scaled_dot_product_attention and logsumexp on the gathered rows;
+  * invariances of the definition: permuting physical pages with the block table,
+    re-expressing a row as a split-and-merge over page-aligned key ranges, and the
+    causal rule that query j of an MTP step equals a q_len = 1 step over its prefix.
+
+The definition being pinned (TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA decode slower
+after #19338", Setup and Repro 1): 576-byte E4M3 rows (512 latent + 64 rope), V = the
+latent, page size 32, scores softmax_scale * q.k, output_scale on O only, and for the
+q = 8 MTP verify step query j attends to KV[0 .. L - 8 + j].
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_gather_amd import inputs
+
+F32_SCALE = float(np.float32(inputs.SOFTMAX_SCALE))
+
+
+def _run(case, lib_path, rows=None, **kw):
+    return oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens,
+                             q_len=case.q_len, num_heads=case.num_heads,
+                             softmax_scale=kw.get("softmax_scale", F32_SCALE),
+                             output_scale=kw.get("output_scale", case.output_scale),
+                             rows=rows, lib_path=lib_path)
+
+
+def _gather(case, b, n):
+    """Gather the first n cached rows of request b with torch indexing -> uint8 [n, 576]."""
+    tok = torch.arange(n)
+    pages = case.block_table[b].to(torch.int64)[tok // inputs.PAGE]
+    return case.kv[pages, tok % inputs.PAGE]
+
+
+def _dec(codes_u8: torch.Tensor) -> torch.Tensor:
+    return codes_u8.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def pin_e4m3_table(lib_path=None):
+    ours = oracle.e4m3_table(lib_path)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    nan_ours, nan_ref = np.isnan(ours), np.isnan(ref)
+    assert (nan_ours == nan_ref).all(), "NaN codes differ"
+    assert nan_ours.sum() == 2 and nan_ours[0x7F] and nan_ours[0xFF]
+    assert np.array_equal(ours[~nan_ours], ref[~nan_ref]), "finite E4M3 values differ"
+    assert np.array_equal(np.signbit(ours[~nan_ours]), np.signbit(ref[~nan_ref]))
+
+
+def pin_single_key(lib_path=None):
+    """kv_len 1: O = output_scale * V_0 exactly and LSE = s_0 (exact rational score)."""
+    case = inputs.make_case([1, 1], num_heads=3, q_len=1, seed=11, output_scale=1.5)
+    o, lse = _run(case, lib_path)
+    tab = [Fraction(v) if not math.isnan(v) else None for v in
+           torch.arange(256).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).tolist()]
+    for b in range(case.batch):
+        k = _gather(case, b, 1)[0]
+        v = _dec(k[:inputs.D_V]).numpy()
+        for h in range(case.num_heads):
+            r = b * case.num_heads + h
+            qrow = case.q[b, 0, h]
+            dot = sum(tab[int(a)] * tab[int(c)] for a, c in zip(qrow.tolist(), k.tolist()))
+            s0 = float(Fraction(F32_SCALE) * dot)
+            assert lse[r] == s0, (lse[r], s0)
+            assert np.array_equal(o[r], 1.5 * v), "O != output_scale * V_0"
+
+
+def pin_equal_scores(lib_path=None):
+    """q = 0 gives equal scores: O is the mean of the visible V rows, LSE = ln n."""
+    case = inputs.make_case([37, 64, 5], num_heads=2, q_len=3, seed=12)
+    case.q.zero_()
+    o, lse = _run(case, lib_path)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        for j in range(case.q_len):
+            n = L - case.q_len + j + 1
+            mean = _dec(_gather(case, b, n)[:, :inputs.D_V]).mean(dim=0).numpy()
+            for h in range(case.num_heads):
+                r = (b * case.q_len + j) * case.num_heads + h
+                np.testing.assert_allclose(o[r], mean, rtol=1e-13, atol=1e-13)
+                assert abs(lse[r] - math.log(n)) <= 1e-14 * max(1.0, math.log(n))
+
+
+def pin_mpmath_bruteforce(lib_path=None):
+    """Tiny inputs against 50-digit arithmetic with no max subtraction."""
+    import mpmath
+    mpmath.mp.dps = 50
+    case = inputs.make_case([3, 8, 2], num_heads=2, q_len=2, seed=13, output_scale=0.75)
+    o, lse = _run(case, lib_path)
+    sc = mpmath.mpf(F32_SCALE)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        for j in range(case.q_len):
+            n = L - case.q_len + j + 1
+            rows = _dec(_gather(case, b, n)).tolist()
+            for h in range(case.num_heads):
+                r = (b * case.q_len + j) * case.num_heads + h
+                qv = _dec(case.q[b, j, h]).tolist()
+                es = []
+                for i in range(n):
+                    dot = mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c) for a, c in zip(qv, rows[i]))
+                    es.append(mpmath.exp(sc * dot))
+                tot = mpmath.fsum(es)
+                ref_lse = float(mpmath.log(tot))
+                assert abs(lse[r] - ref_lse) <= 1e-13 * max(1.0, abs(ref_lse)), (lse[r], ref_lse)
+                for d in range(0, inputs.D_V, 7):
+                    ref = float(mpmath.mpf("0.75") *
+                                mpmath.fsum(es[i] * rows[i][d] for i in range(n)) / tot)
+                    assert abs(o[r, d] - ref) <= 1e-13 * max(1.0, abs(ref)), (d, o[r, d], ref)
+
+
+def pin_sdpa(lib_path=None):
+    """fp64 torch SDPA (causal within the q_len queries) + logsumexp on gathered rows."""
+    case = inputs.make_case([3, 33, 64, 100], num_heads=4, q_len=3, seed=14)
+    o, lse = _run(case, lib_path)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        kfull = _dec(_gather(case, b, L))                      # [L, 576]
+        qb = _dec(case.q[b]).permute(1, 0, 2).contiguous()      # [H, q, 576]
+        k = kfull.unsqueeze(0).expand(case.num_heads, L, inputs.D_QK).contiguous()
+        v = kfull[:, :inputs.D_V].unsqueeze(0).expand(case.num_heads, L, inputs.D_V).contiguous()
+        pos = torch.arange(L)
+        jj = torch.arange(case.q_len).unsqueeze(1)
+        mask = pos.unsqueeze(0) <= (L - case.q_len + jj)        # [q, L]
+        out = torch.nn.functional.scaled_dot_product_attention(
+            qb, k, v, attn_mask=mask, scale=F32_SCALE)          # [H, q, 512]
+        scores = (qb @ k.transpose(1, 2)) * F32_SCALE
+        scores = scores.masked_fill(~mask, float("-inf"))
+        ref_lse = torch.logsumexp(scores, dim=-1)               # [H, q]
+        for j in range(case.q_len):
+            for h in range(case.num_heads):
+                r = (b * case.q_len + j) * case.num_heads + h
+                np.testing.assert_allclose(o[r], out[h, j].numpy(), rtol=1e-12, atol=1e-12)
+                assert abs(lse[r] - float(ref_lse[h, j])) <= 1e-12 * max(1.0, abs(lse[r]))
+
+
+def pin_page_permutation(lib_path=None):
+    """Moving physical pages (and their block-table entries) changes nothing, bitwise."""
+    case = inputs.make_case([70, 129], num_heads=3, q_len=2, seed=15)
+    o1, l1 = _run(case, lib_path)
+    g = torch.Generator().manual_seed(99)
+    P = case.num_pages
+    perm = torch.randperm(P, generator=g)           # new position of old page p
+    kv2 = torch.empty_like(case.kv)
+    kv2[perm] = case.kv
+    bt2 = perm.to(torch.int32)[case.block_table.to(torch.int64)]
+    case2 = inputs.Case(q=case.q, kv=kv2, block_table=bt2, kv_lens=case.kv_lens,
+                        q_len=case.q_len, num_heads=case.num_heads)
+    o2, l2 = _run(case2, lib_path)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_causal_prefix(lib_path=None):
+    """Query j of a q_len-token step equals a q_len = 1 step over KV[0 .. L - q_len + j]."""
+    case = inputs.make_case([96, 45], num_heads=2, q_len=4, seed=16)
+    o, lse = _run(case, lib_path)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        for j in range(case.q_len):
+            n = L - case.q_len + j + 1
+            single = inputs.Case(q=case.q[b:b + 1, j:j + 1].contiguous(), kv=case.kv,
+                                 block_table=case.block_table[b:b + 1].contiguous(),
+                                 kv_lens=torch.tensor([n], dtype=torch.int32), q_len=1,
+                                 num_heads=case.num_heads)
+            o1, l1 = _run(single, lib_path)
+            for h in range(case.num_heads):
+                r = (b * case.q_len + j) * case.num_heads + h
+                assert np.array_equal(o[r], o1[h]) and lse[r] == l1[h], (b, j, h)
+
+
+def pin_split_merge(lib_path=None):
+    """Page-aligned key ranges run as separate requests, merged in fp64 with
+    weights exp(LSE_s - LSE), reproduce the unsplit row (the split-KV identity)."""
+    L = 200
+    case = inputs.make_case([L], num_heads=2, q_len=1, seed=17)
+    o, lse = _run(case, lib_path)
+    for bounds in ([0, 32, 200], [0, 64, 96, 160, 200], [0, 192, 200]):
+        outs, lses = [], []
+        for a, e in zip(bounds[:-1], bounds[1:]):
+            sub = inputs.Case(q=case.q, kv=case.kv,
+                              block_table=case.block_table[:, a // 32:].contiguous(),
+                              kv_lens=torch.tensor([e - a], dtype=torch.int32), q_len=1,
+                              num_heads=case.num_heads)
+            os_, ls_ = _run(sub, lib_path)
+            outs.append(os_)
+            lses.append(ls_)
+        lses = np.stack(lses)                       # [S, rows]
+        tot = np.logaddexp.reduce(lses, axis=0)
+        w = np.exp(lses - tot)                      # [S, rows]
+        merged = sum(w[s][:, None] * outs[s] for s in range(len(outs)))
+        np.testing.assert_allclose(merged, o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(tot, lse, rtol=1e-13, atol=1e-13)
+
+
+def pin_bounds_and_dominant(lib_path=None):
+    """max s <= LSE <= max s + ln n; one overwhelming key pulls O onto its V row."""
+    case = inputs.make_case([300], num_heads=2, q_len=1, seed=18)
+    o, lse = _run(case, lib_path)
+    kfull = _dec(_gather(case, 0, 300))
+    for h in range(2):
+        s = (kfull @ _dec(case.q[0, 0, h])) * F32_SCALE
+        assert float(s.max()) <= lse[h] <= float(s.max()) + math.log(300) + 1e-12
+    # make key 123 dominant for head 0: q = that key's codes, large scale
+    case.q[0, 0, 0] = _gather(case, 0, 300)[123]
+    o, lse = _run(case, lib_path, softmax_scale=10.0)
+    v123 = _dec(_gather(case, 0, 300)[123, :inputs.D_V]).numpy()
+    np.testing.assert_allclose(o[0], v123, rtol=0, atol=1e-6)
+
+
+ALL_PINS = [pin_e4m3_table, pin_single_key, pin_equal_scores, pin_mpmath_bruteforce,
+            pin_sdpa, pin_page_permutation, pin_causal_prefix, pin_split_merge,
+            pin_bounds_and_dominant]

@@ -1,0 +1,53 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and show that the
+pins catch each one. The copy is built in a temporary directory; the real oracle is
+untouched."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "mla_oracle.c")
+
+# (name, text in mla_oracle.c, replacement)
+MUTANTS = [
+    ("causal_off_by_one", "int64_t n = L - J->q_len + j + 1;", "int64_t n = L - J->q_len + j;"),
+    ("drop_rope", "for (int d = 0; d < ORACLE_D_QK; ++d) dot +=",
+     "for (int d = 0; d < ORACLE_D_V; ++d) dot +="),
+    ("wrong_slot", "(page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;\n    double dot",
+     "(page * ORACLE_PAGE + (i + 1) % ORACLE_PAGE) * ORACLE_D_QK;\n    double dot"),
+    ("log2_lse", "J->out_lse[idx] = m + log(l);", "J->out_lse[idx] = m + log2(l);"),
+    ("scale_on_lse", "J->out_lse[idx] = m + log(l);",
+     "J->out_lse[idx] = m + log(l) + log(J->output_scale);"),
+    ("subnormal_exponent", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
+    ("v_from_rope", "acc[d] += w * J->table[v[d]];", "acc[d] += w * J->table[v[d + 64]];"),
+    ("no_max_shift_sign", "double w = exp(s[i] - m);", "double w = exp(m - s[i]);"),
+]
+
+
+def _build_mutant(tmpdir, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    path_c = os.path.join(tmpdir, "mutant.c")
+    path_so = os.path.join(tmpdir, "libmutant.so")
+    with open(path_c, "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared", "-pthread",
+                    "-o", path_so, path_c, "-lm"], check=True)
+    return path_so
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new):
+    with tempfile.TemporaryDirectory() as d:
+        lib = _build_mutant(d, old, new)
+        caught = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(lib_path=lib)
+            except (AssertionError, ValueError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin caught mutant {name}"
