@@ -1,0 +1,137 @@
+// C-ABI entry points of libmla_decode.so: argument checks on the host, then the two
+// kernel launches on the caller's stream. Nothing here allocates device memory or
+// synchronises; every check runs before the first launch, so a rejected call enqueues
+// nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+int query_num_cus(int32_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return MLA_ERR_HIP_BASE - (int)e;
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return MLA_ERR_HIP_BASE - (int)e;
+  if (n <= 0) return MLA_ERR_HIP_BASE - (int)hipErrorInvalidDevice;
+  *out = n;
+  return MLA_OK;
+}
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_workspace(const mla_decode_plan_s* plan, const void* ws, size_t bytes) {
+  if (ws == nullptr || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
+  if (bytes < plan->ws_o_bytes + plan->ws_stats_bytes) return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+int check_partial(const mla_decode_plan_s* plan, const void* q, const void* kv,
+                  const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                  float softmax_scale, const void* ws, size_t ws_bytes) {
+  if (plan == nullptr || q == nullptr || kv == nullptr || bt == nullptr || kv_lens == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(bt, 4) || !aligned(kv_lens, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || __builtin_isinf(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  // every request's pages must fit its block-table row
+  int64_t max_pages = 0;
+  for (int32_t b = 0; b < plan->dev.batch; ++b) {
+    const int64_t p = ((int64_t)plan->kv_lens[b] + kPage - 1) / kPage;
+    if (p > max_pages) max_pages = p;
+  }
+  if (bt_stride < max_pages) return MLA_ERR_INVALID_ARG;
+  return check_workspace(plan, ws, ws_bytes);
+}
+
+int check_merge(const mla_decode_plan_s* plan, const void* ws, size_t ws_bytes,
+                float output_scale, const void* o, const float* lse) {
+  if (plan == nullptr || o == nullptr) return MLA_ERR_INVALID_ARG;
+  if (!aligned(o, 4) || (lse != nullptr && !aligned(lse, 4))) return MLA_ERR_INVALID_ARG;
+  if (!(output_scale == output_scale) || __builtin_isinf(output_scale))
+    return MLA_ERR_INVALID_ARG;
+  return check_workspace(plan, ws, ws_bytes);
+}
+
+int hip_status(int e) { return e == (int)hipSuccess ? MLA_OK : MLA_ERR_HIP_BASE - e; }
+
+float* ws_o_of(const mla_decode_plan_s* plan, const void* ws) { return (float*)ws; }
+float* ws_stats_of(const mla_decode_plan_s* plan, const void* ws) {
+  return (float*)((uint8_t*)ws + plan->ws_o_bytes);
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+int mla_decode_partial(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride,
+                       const int32_t* kv_lens, float softmax_scale, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
+                         workspace, workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                   block_table, bt_stride, kv_lens, softmax_scale,
+                                   ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                   stream));
+}
+
+int mla_decode_merge(const mla_decode_plan_t* plan, const void* workspace,
+                     size_t workspace_bytes, float output_scale, void* o, float* lse,
+                     void* stream) {
+  int rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 output_scale, o, false, lse, stream));
+}
+
+int mla_decode_merge_f32(const mla_decode_plan_t* plan, const void* workspace,
+                         size_t workspace_bytes, float output_scale, float* o, float* lse,
+                         void* stream) {
+  int rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 output_scale, o, true, lse, stream));
+}
+
+int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+               const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+               float softmax_scale, float output_scale, void* workspace,
+               size_t workspace_bytes, void* o, float* lse, void* stream) {
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
+                         workspace, workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                 block_table, bt_stride, kv_lens, softmax_scale,
+                                 ws_o_of(plan, workspace), ws_stats_of(plan, workspace), stream));
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 output_scale, o, false, lse, stream));
+}
+
+const char* mla_decode_strerror(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (batch, rows per request or split cap)";
+    case MLA_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or smaller than mla_decode_workspace_size()";
+    case MLA_ERR_NOMEM: return "host allocation failed";
+    default: break;
+  }
+  if (status <= MLA_ERR_HIP_BASE) return hipGetErrorString((hipError_t)(MLA_ERR_HIP_BASE - status));
+  return "unknown status";
+}
+
+}  // extern "C"

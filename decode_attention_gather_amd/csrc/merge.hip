@@ -1,0 +1,142 @@
+// Merge kernel: combines each row's split partials into BF16 (or fp32) O and fp32 LSE.
+//
+// Method of TensorRT-LLM PR #20380 "trtllm-gen FMHA: split the KV partials of a row
+// across thread groups in fmhaReductionKernel" (Description), re-done for 64-wide
+// wavefronts: one workgroup per row with G wavefront groups; group g folds partials
+// g, g + G, ... with the online-softmax merge, then the groups are combined through LDS,
+// each scaled by 2^(group max - max) and empty groups skipped. Each lane owns 8 of the
+// 512 output dims, so every partial row is one fully coalesced 2 KB read per wavefront.
+//
+// Partials arrive from the split-KV kernel as (m, l, l~, O) with m an integer (log2
+// units), so every rescale here is an exact power of two (v_ldexp_f32):
+//     M = max_s m_s,  O = sum_s 2^(m_s - M) O_s,  l = sum_s 2^(m_s - M) l_s  (same for l~)
+//     out = output_scale * O / l~,   LSE = ln(2) * (M - 8 + log2(l))
+// (the 8 undoes the 2^8 scale of the partials' probabilities). A partial with m = -inf
+// (a split in which a causal row sees no key) contributes nothing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kMaxGroups = 16;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ float pow2i(float m_from, float m_to) {
+  // 2^(m_from - m_to) for integer-valued m_from <= m_to; 0 when m_from is -inf
+  return m_from == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m_from - m_to));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct MergeSmem {
+  float o[kMaxGroups][kDV];
+  float m[kMaxGroups];
+  float l[kMaxGroups];
+  float lt[kMaxGroups];
+};
+
+template <bool kF32Out>
+__global__ void __launch_bounds__(64 * kMaxGroups)
+merge_kernel(const PlanDev P, const float* __restrict__ ws_o, const float* __restrict__ ws_stats,
+             float output_scale, void* __restrict__ out, float* __restrict__ lse, int groups) {
+  __shared__ MergeSmem sm;
+  const int row_global = blockIdx.x;  // (b * q_len + j) * H + h
+  const int b = row_global / P.rows;
+  const int r = row_global - b * P.rows;
+  const int S = P.splits[b];
+  const int base = (int)P.part_base[b];
+  const int lane = threadIdx.x & 63;
+  const int gw = threadIdx.x >> 6;
+
+  float M = -INFINITY, l = 0.f, lt = 0.f;
+  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+  for (int s0 = gw; s0 < S; s0 += kUnroll * groups) {
+    float4 stv[kUnroll], a[kUnroll], c[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + u * groups;
+      if (s < S) {
+        const int64_t pr = (int64_t)(base + s) * P.rows + r;
+        stv[u] = *(const float4*)(ws_stats + pr * kStatStride);
+        const float4* op = (const float4*)(ws_o + pr * kDV) + 2 * lane;
+        a[u] = op[0];
+        c[u] = op[1];
+      } else {
+        stv[u] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+        a[u] = c[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float ms = stv[u].x;
+      if (ms == -INFINITY) continue;
+      const float Mn = fmaxf(M, ms);
+      const float wa = pow2i(M, Mn), wb = pow2i(ms, Mn);
+      o0.x = o0.x * wa + a[u].x * wb; o0.y = o0.y * wa + a[u].y * wb;
+      o0.z = o0.z * wa + a[u].z * wb; o0.w = o0.w * wa + a[u].w * wb;
+      o1.x = o1.x * wa + c[u].x * wb; o1.y = o1.y * wa + c[u].y * wb;
+      o1.z = o1.z * wa + c[u].z * wb; o1.w = o1.w * wa + c[u].w * wb;
+      l = l * wa + stv[u].y * wb;
+      lt = lt * wa + stv[u].z * wb;
+      M = Mn;
+    }
+  }
+  float4* so = (float4*)sm.o[gw] + 2 * lane;
+  so[0] = o0;
+  so[1] = o1;
+  if (lane == 0) {
+    sm.m[gw] = M;
+    sm.l[gw] = l;
+    sm.lt[gw] = lt;
+  }
+  __syncthreads();
+
+  float Mx = -INFINITY;
+  for (int k = 0; k < groups; ++k) Mx = fmaxf(Mx, sm.m[k]);
+  float wk[kMaxGroups];
+  float L = 0.f, Lt = 0.f;
+  for (int k = 0; k < groups; ++k) {
+    wk[k] = Mx == -INFINITY ? 0.f : pow2i(sm.m[k], Mx);
+    L += wk[k] * sm.l[k];
+    Lt += wk[k] * sm.lt[k];
+  }
+  const float inv = Lt > 0.f ? output_scale / Lt : 0.f;
+  for (int d = threadIdx.x; d < kDV; d += 64 * groups) {
+    float acc = 0.f;
+    for (int k = 0; k < groups; ++k) acc += wk[k] * sm.o[k][d];
+    const float v = acc * inv;
+    if (kF32Out)
+      ((float*)out)[(int64_t)row_global * kDV + d] = v;
+    else
+      ((uint16_t*)out)[(int64_t)row_global * kDV + d] = f32_to_bf16_rne(v);
+  }
+  if (lse != nullptr && threadIdx.x == 0)
+    lse[row_global] = L > 0.f ? 0.69314718055994531f * ((Mx - 8.f) + log2f(L)) : -INFINITY;
+}
+
+}  // namespace
+
+int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
+                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream) {
+  const PlanDev& P = plan.dev;
+  const int rows_total = P.batch * P.rows;
+  const int groups = plan.merge_groups;
+  if (o_is_f32)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(rows_total), dim3(64 * groups), 0,
+                       (hipStream_t)stream, P, ws_o, ws_stats, output_scale, o, lse, groups);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(rows_total), dim3(64 * groups), 0,
+                       (hipStream_t)stream, P, ws_o, ws_stats, output_scale, o, lse, groups);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla

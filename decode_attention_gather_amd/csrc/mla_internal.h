@@ -1,0 +1,79 @@
+// Internal types shared by the planner, the C-ABI layer and the two kernels of
+// libmla_decode.so. Not installed; the public interface is include/mla_decode.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla_decode.h"
+
+#ifndef __HIPCC__
+#define __host__
+#define __device__
+#endif
+
+namespace mla {
+
+constexpr int kDQK = MLA_D_QK;             // 576 bytes per cached row
+constexpr int kDV = MLA_D_V;               // 512 latent = V = O width
+constexpr int kPage = MLA_PAGE_SIZE;       // 32 tokens per page
+constexpr int kPageBytes = kPage * kDQK;   // 18432
+constexpr int kTileRows = 16;              // query rows per MFMA row tile
+constexpr int kMaxTilesPerBlock = 4;      // row tiles per workgroup (64 rows)
+constexpr int kMaxBatch = MLA_MAX_BATCH;
+constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
+constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
+
+// Everything the kernels need from a plan, passed by value as a kernel argument
+// (3.6 KB, under the 4 KB kernel-argument limit). Requests are issued longest split
+// first: sorted entry e holds (running split count through e) << 8 | request id.
+// Pages per split of request b are ceil(ceil(kv_len[b] / 32) / splits[b]); the kernels
+// clamp every key range to the plan's kv_len, so a larger device length cannot make
+// them read past the block-table row the plan was checked against.
+struct PlanDev {
+  int32_t batch;
+  int32_t q_len;
+  int32_t heads;
+  int32_t rows;         // q_len * heads, rows per request
+  int32_t tiles;        // row blocks (workgroups) per split: ceil(rows / (16 nt))
+  int32_t total_parts;  // sum of splits
+  int32_t nt;           // 16-row tiles per row block, 1..4
+  int32_t pad1;
+  uint32_t sorted[kMaxBatch];     // (part_end << 8) | request
+  uint32_t kv_len[kMaxBatch];     // per request: the plan's (host) length
+  uint32_t part_base[kMaxBatch];  // per request: index of its first split
+  uint16_t splits[kMaxBatch];     // per request
+};
+static_assert(sizeof(PlanDev) <= 3800, "kernel argument budget");
+
+__host__ __device__ inline int chunk_pages_of(const PlanDev& P, int b) {
+  const int pages = (int)((P.kv_len[b] + kPage - 1) / kPage);
+  return (pages + P.splits[b] - 1) / P.splits[b];
+}
+
+}  // namespace mla
+
+// Host-side plan object (opaque to callers).
+struct mla_decode_plan_s {
+  mla::PlanDev dev;
+  int32_t merge_groups;
+  int32_t max_splits;
+  int32_t num_cus;
+  size_t ws_o_bytes;      // fp32 partial O region
+  size_t ws_stats_bytes;  // fp32 (m, l, l~, 0) region
+  int32_t* kv_lens;       // host copy [batch]
+};
+
+namespace mla {
+
+// Workspace carve-up: partial O at offset 0, stats after it (256-byte aligned).
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Launchers (defined next to their kernels). Return a hipError_t value as int.
+int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                   const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                   float softmax_scale, float* ws_o, float* ws_stats, void* stream);
+int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
+                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream);
+
+}  // namespace mla

@@ -1,0 +1,186 @@
+// Host split planner for split-KV MLA decode.
+//
+// Prior art: the per-request split plan of TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA
+// decode slower after #19338" (Repro 2: block_split_kvs from the planner, a per-request
+// cap raised to 128 "so that one request can fill the GPU"; follow-up comment: the plan
+// clamped to [1, split_kv], and a minimum split length of one tile rather than four at
+// short KV) and the grid rule of its Repro 1 (uniform split_kv so that B * split_kv is
+// about one wave). Here a wave is one workgroup per CU on a 256-CU MI355X, and a work
+// item is one (split, 16-row tile); the merge-width rule follows PR #20380 "trtllm-gen
+// FMHA: split the KV partials of a row across thread groups in fmhaReductionKernel"
+// (Description: an upper bound halved until the launch fits a 2-per-CU budget).
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+int query_num_cus(int32_t* out);  // abi.hip (HIP runtime)
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Splits wanted per request before clamping.
+void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t max_split,
+                 int32_t tiles, int32_t num_cus, std::vector<int64_t>& want) {
+  const size_t B = pages.size();
+  want.assign(B, 1);
+  if (split_kv > 0) {
+    for (size_t b = 0; b < B; ++b) want[b] = std::min<int64_t>(split_kv, max_split);
+    return;
+  }
+  // Proportional plan: sum_b S_b * tiles ~= num_cus, S_b proportional to the pages of
+  // request b, so every work item streams about the same number of pages.
+  int64_t total = 0;
+  for (int64_t p : pages) total += p;
+  const double items_per_page = (double)num_cus / ((double)tiles * (double)total);
+  for (size_t b = 0; b < B; ++b) {
+    int64_t s = (int64_t)(items_per_page * (double)pages[b]);  // floor: at most one wave
+    want[b] = std::max<int64_t>(1, std::min<int64_t>(s, max_split));
+  }
+}
+
+}  // namespace
+
+int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
+               int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+               mla_decode_plan_s** out) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (kv_lens_host == nullptr || batch < 1 || q_len < 1 || num_heads < 1 || split_kv < 0 ||
+      max_split_kv < 1 || num_cus < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (batch > kMaxBatch || max_split_kv > MLA_MAX_SPLIT_KV ||
+      (int64_t)q_len * num_heads > MLA_MAX_ROWS_PER_REQUEST)
+    return MLA_ERR_UNSUPPORTED_SHAPE;
+  for (int32_t b = 0; b < batch; ++b)
+    if (kv_lens_host[b] < q_len) return MLA_ERR_INVALID_ARG;
+  if (num_cus == 0) {
+    int rc = query_num_cus(&num_cus);
+    if (rc != MLA_OK) return rc;
+  }
+
+  const int32_t rows = q_len * num_heads;
+  // Row blocks: at most 4 MFMA row tiles (64 rows) per workgroup, balanced, so that one
+  // staged page feeds as many rows as the workgroup's registers hold.
+  const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
+  const int32_t tiles = (int32_t)ceil_div(tiles16, kMaxTilesPerBlock);
+  const int32_t nt = (int32_t)ceil_div(tiles16, tiles);
+  std::vector<int64_t> pages(batch), want;
+  for (int32_t b = 0; b < batch; ++b) pages[b] = ceil_div(kv_lens_host[b], kPage);
+  want_splits(pages, split_kv, max_split_kv, tiles, num_cus, want);
+
+  auto* plan = new (std::nothrow) mla_decode_plan_s();
+  if (plan == nullptr) return MLA_ERR_NOMEM;
+  plan->kv_lens = (int32_t*)std::malloc(sizeof(int32_t) * batch);
+  if (plan->kv_lens == nullptr) {
+    delete plan;
+    return MLA_ERR_NOMEM;
+  }
+  std::memcpy(plan->kv_lens, kv_lens_host, sizeof(int32_t) * batch);
+
+  PlanDev& d = plan->dev;
+  std::memset(&d, 0, sizeof(d));
+  d.batch = batch;
+  d.q_len = q_len;
+  d.heads = num_heads;
+  d.rows = rows;
+  d.tiles = tiles;
+  d.nt = nt;
+
+  int64_t total = 0, max_s = 0;
+  std::vector<int64_t> chunk_of(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    // whole pages per split, no empty split, split length within uint16 pages
+    int64_t s = std::max<int64_t>(1, std::min<int64_t>(want[b], pages[b]));
+    s = std::max<int64_t>(s, ceil_div(pages[b], kMaxChunkPages));
+    int64_t chunk = ceil_div(pages[b], s);
+    s = ceil_div(pages[b], chunk);
+    d.splits[b] = (uint16_t)s;
+    d.kv_len[b] = (uint32_t)kv_lens_host[b];
+    d.part_base[b] = (uint32_t)total;
+    chunk_of[b] = chunk;
+    total += s;
+    max_s = std::max(max_s, s);
+  }
+  if (total * tiles > INT32_MAX / 2 || total >= (1 << 23)) {
+    mla_decode_plan_destroy(plan);
+    return MLA_ERR_UNSUPPORTED_SHAPE;
+  }
+  d.total_parts = (int32_t)total;
+
+  // Longest request first, so the longest work items start in the first wave.
+  std::vector<int32_t> order(batch);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return chunk_of[a] > chunk_of[b]; });
+  uint32_t run = 0;
+  for (int32_t e = 0; e < batch; ++e) {
+    run += d.splits[order[e]];
+    d.sorted[e] = (run << 8) | (uint32_t)order[e];
+  }
+
+  // Merge width: wavefront groups per row, a power of two <= min(16, max splits),
+  // halved while rows * groups exceeds 8 waves per CU.
+  int32_t g = 1;
+  while (g * 2 <= 16 && g * 2 <= max_s) g *= 2;
+  const int64_t rows_total = (int64_t)batch * rows;
+  while (g > 1 && rows_total * g > 8LL * num_cus) g /= 2;
+  plan->merge_groups = g;
+  plan->max_splits = (int32_t)max_s;
+  plan->num_cus = num_cus;
+  plan->ws_o_bytes = align256((size_t)total * rows * kDV * sizeof(float));
+  plan->ws_stats_bytes = align256((size_t)total * rows * kStatStride * sizeof(float));
+  *out = plan;
+  return MLA_OK;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
+                    int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
+                    int32_t num_cus, mla_decode_plan_t** out) {
+  return mla::build_plan(kv_lens_host, batch, q_len, num_heads, split_kv, max_split_kv,
+                         num_cus, out);
+}
+
+void mla_decode_plan_destroy(mla_decode_plan_t* plan) {
+  if (plan == nullptr) return;
+  std::free(plan->kv_lens);
+  delete plan;
+}
+
+size_t mla_decode_workspace_size(const mla_decode_plan_t* plan) {
+  if (plan == nullptr) return 0;
+  return plan->ws_o_bytes + plan->ws_stats_bytes;
+}
+
+int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,
+                             int32_t* splits, int32_t* chunk_tokens) {
+  if (plan == nullptr || info == nullptr) return MLA_ERR_INVALID_ARG;
+  const mla::PlanDev& d = plan->dev;
+  info->batch = d.batch;
+  info->q_len = d.q_len;
+  info->num_heads = d.heads;
+  info->rows_per_request = d.rows;
+  info->row_tiles = d.tiles;
+  info->total_splits = d.total_parts;
+  info->work_items = d.total_parts * d.tiles;
+  info->merge_groups = plan->merge_groups;
+  info->max_splits = plan->max_splits;
+  for (int32_t b = 0; b < d.batch; ++b) {
+    if (splits) splits[b] = d.splits[b];
+    if (chunk_tokens) chunk_tokens[b] = mla::chunk_pages_of(d, b) * mla::kPage;
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

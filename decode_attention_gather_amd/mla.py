@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libmla_decode.so (declared in include/mla_decode.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels. Tensors are PyTorch tensors used as device buffers (``data_ptr()``); the
+stream defaults to PyTorch's current stream. Importing this module raises if the
+built library is missing — there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED_SHAPE = -2
+MLA_ERR_WORKSPACE = -3
+MLA_ERR_NOMEM = -4
+MLA_ERR_HIP_BASE = -1000
+
+D_QK, D_V, PAGE = 576, 512, 32
+
+EXPORTS = [
+    "mla_decode_plan", "mla_decode_plan_destroy", "mla_decode_workspace_size",
+    "mla_decode_plan_get_info", "mla_decode_partial", "mla_decode_merge",
+    "mla_decode_merge_f32", "mla_decode", "mla_decode_strerror",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m decode_attention_gather_amd.build` "
+        "(hipcc, gfx950). There is no non-HIP fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("q_len", _i32), ("num_heads", _i32),
+                ("rows_per_request", _i32), ("row_tiles", _i32), ("total_splits", _i32),
+                ("work_items", _i32), ("merge_groups", _i32), ("max_splits", _i32)]
+
+
+_lib.mla_decode_plan.restype = ctypes.c_int
+_lib.mla_decode_plan.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
+_lib.mla_decode_plan_destroy.restype = None
+_lib.mla_decode_plan_destroy.argtypes = [_p]
+_lib.mla_decode_workspace_size.restype = _sz
+_lib.mla_decode_workspace_size.argtypes = [_p]
+_lib.mla_decode_plan_get_info.restype = ctypes.c_int
+_lib.mla_decode_plan_get_info.argtypes = [_p, ctypes.POINTER(PlanInfo), _p, _p]
+_lib.mla_decode_partial.restype = ctypes.c_int
+_lib.mla_decode_partial.argtypes = [_p, _p, _p, _p, _i64, _p, _f32, _p, _sz, _p]
+_lib.mla_decode_merge.restype = ctypes.c_int
+_lib.mla_decode_merge.argtypes = [_p, _p, _sz, _f32, _p, _p, _p]
+_lib.mla_decode_merge_f32.restype = ctypes.c_int
+_lib.mla_decode_merge_f32.argtypes = [_p, _p, _sz, _f32, _p, _p, _p]
+_lib.mla_decode.restype = ctypes.c_int
+_lib.mla_decode.argtypes = [_p, _p, _p, _p, _i64, _p, _f32, _f32, _p, _sz, _p, _p, _p]
+_lib.mla_decode_strerror.restype = ctypes.c_char_p
+_lib.mla_decode_strerror.argtypes = [ctypes.c_int]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def strerror(status: int) -> str:
+    return _lib.mla_decode_strerror(int(status)).decode()
+
+
+def lib_handle():
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != MLA_OK:
+        raise MlaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Plan:
+    """Owns an mla_decode_plan_t; freed on close() / garbage collection."""
+
+    def __init__(self, kv_lens: Sequence[int], *, q_len: int, num_heads: int, split_kv: int = 0,
+                 max_split_kv: int = 128, num_cus: int = 0):
+        lens = (ctypes.c_int32 * len(kv_lens))(*[int(x) for x in kv_lens])
+        h = ctypes.c_void_p()
+        _check(_lib.mla_decode_plan(lens, len(kv_lens), q_len, num_heads, split_kv, max_split_kv,
+                                    num_cus, ctypes.byref(h)), "mla_decode_plan")
+        self._h = h
+        self.batch = len(kv_lens)
+        self.q_len = q_len
+        self.num_heads = num_heads
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.mla_decode_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def workspace_size(self) -> int:
+        return int(_lib.mla_decode_workspace_size(self._h))
+
+    def info(self):
+        inf = PlanInfo()
+        splits = (ctypes.c_int32 * self.batch)()
+        chunk = (ctypes.c_int32 * self.batch)()
+        _check(_lib.mla_decode_plan_get_info(self._h, ctypes.byref(inf), splits, chunk),
+               "mla_decode_plan_get_info")
+        return inf, list(splits), list(chunk)
+
+    def alloc_workspace(self, device="cuda") -> torch.Tensor:
+        # torch's caching allocator returns 256-byte aligned blocks
+        return torch.empty(max(1, self.workspace_size()), dtype=torch.uint8, device=device)
+
+
+def partial(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float, workspace,
+            stream=None):
+    _check(_lib.mla_decode_partial(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                   block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_decode_partial")
+
+
+def merge(plan: Plan, workspace, output_scale: float, o, lse=None, stream=None):
+    fn = _lib.mla_decode_merge_f32 if o.dtype == torch.float32 else _lib.mla_decode_merge
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("o must be bfloat16 or float32")
+    _check(fn(plan.handle, _ptr(workspace), workspace.numel(), float(output_scale), _ptr(o),
+              _ptr(lse), _stream(stream)), "mla_decode_merge")
+
+
+def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
+           output_scale: float, workspace, o, lse=None, stream=None):
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    _check(_lib.mla_decode(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                           block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
+                           float(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
+                           _ptr(lse), _stream(stream)), "mla_decode")
+
+
+@dataclass
+class DeviceCase:
+    """A decode batch resident on the GPU (see decode_attention_gather_amd.inputs.Case)."""
+    q: torch.Tensor
+    kv: torch.Tensor
+    block_table: torch.Tensor
+    kv_lens: torch.Tensor
+    kv_lens_host: List[int]
+    q_len: int
+    num_heads: int
+    softmax_scale: float
+    output_scale: float
+
+
+def to_device(case, device="cuda") -> DeviceCase:
+    return DeviceCase(q=case.q.to(device), kv=case.kv.to(device),
+                      block_table=case.block_table.to(device), kv_lens=case.kv_lens.to(device),
+                      kv_lens_host=[int(x) for x in case.kv_lens.tolist()], q_len=case.q_len,
+                      num_heads=case.num_heads, softmax_scale=case.softmax_scale,
+                      output_scale=case.output_scale)
+
+
+def run_decode(dc: DeviceCase, plan: Plan, workspace=None, f32_out: bool = False):
+    """Run partial + merge; returns (O [B*q*H, 512], LSE [B*q*H])."""
+    rows = len(dc.kv_lens_host) * dc.q_len * dc.num_heads
+    dev = dc.q.device
+    if workspace is None:
+        workspace = plan.alloc_workspace(dev)
+    o = torch.empty((rows, D_V), dtype=torch.float32 if f32_out else torch.bfloat16, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    if f32_out:
+        partial(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale, workspace)
+        merge(plan, workspace, dc.output_scale, o, lse)
+    else:
+        decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+               dc.output_scale, workspace, o, lse)
+    return o, lse

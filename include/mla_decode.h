@@ -1,0 +1,165 @@
+/*
+ * mla_decode.h - C ABI of libmla_decode.so: split-KV (flash-decoding) MLA decode
+ * attention over a paged FP8 E4M3 KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Operation. Each cached token is one 576-byte row of OCP FP8 E4M3 values: a 512-wide
+ * latent followed by a 64-wide rope part; the cache is paged, 32 tokens per page; V is
+ * the 512-wide latent of the same row (geometry and dtypes as in TensorRT-LLM issue
+ * #20510 "CuTe DSL FP8 MLA decode slower after #19338", Setup). For request b with
+ * KV length L_b and q_len query tokens, query token j attends causally to KV tokens
+ * 0 .. L_b - q_len + j (the q = 8 "MTP verify" shape of the same Setup; q_len = 1 sees
+ * all L_b). With s_i = softmax_scale * (q . K_i) over all 576 dims:
+ *     O   = output_scale * sum_i exp(s_i) V_i / sum_i exp(s_i)      (BF16 out)
+ *     LSE = ln sum_i exp(s_i)                                       (fp32 out)
+ * softmax_scale and output_scale are the two scale arguments of the kernel module's
+ * run() in that issue's Repro 1. LSE is the softmax statistic that the module can emit
+ * (emit_softmax_stats, lse_dtype Float32 in the same listing); it excludes output_scale.
+ *
+ * Method. The host planner (mla_decode_plan) cuts each request's keys into S_b splits
+ * of whole pages. mla_decode_partial runs one workgroup per (split, block of <= 64
+ * query rows) and
+ * writes, per (row, split), an online-softmax partial (max, sum, unnormalised O) in
+ * fp32; mla_decode_merge combines each row's partials, with groups of wavefronts
+ * folding interleaved subsets of them and rescaling each group result by
+ * 2^(group max - max) before the final combine (the KvSplit thread-group merge of
+ * TensorRT-LLM PR #20380 "trtllm-gen FMHA: split the KV partials of a row across thread
+ * groups in fmhaReductionKernel", Description, re-done for 64-wide wavefronts).
+ * Splitting changes nothing beyond rounding: partial maxima are kept on integers (log2
+ * units) so every rescale is an exact power of two.
+ *
+ * Layouts (all row-major, contiguous, device memory owned by the caller):
+ *   q            uint8 E4M3 codes [B][q_len][H][576]
+ *   kv_cache     uint8 E4M3 codes [num_pages][32][576]
+ *   block_table  int32 [B][bt_stride]; entry p of request b is the cache page holding
+ *                tokens 32p .. 32p+31; only entries p < ceil(L_b / 32) are read
+ *   kv_lens      int32 [B] (device copy of the lengths given to the plan)
+ *   o            BF16 [B][q_len][H][512]   (or fp32 for mla_decode_merge_f32)
+ *   lse          fp32 [B][q_len][H]        (may be NULL)
+ *   workspace    caller-allocated device scratch of mla_decode_workspace_size() bytes,
+ *                256-byte aligned; it carries the partials from partial to merge
+ * Flat row id: r = (b * q_len + j) * H + h.
+ *
+ * Threading and streams. A plan is immutable after creation and may be shared by
+ * threads. All compute calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ * null stream), enqueue nothing else, and never synchronise the host. The library
+ * allocates no device memory, keeps no global mutable state, and throws nothing.
+ *
+ * Errors. Every int-returning call returns MLA_OK (0) or a negative status. Argument,
+ * shape and workspace checks run on the host before anything is enqueued, so a failed
+ * call writes nothing. A HIP launch failure returns MLA_ERR_HIP_BASE - hipError_t.
+ * Device-side preconditions that are not checked: block-table entries below
+ * ceil(L_b / 32) must be valid page indices, and the device kv_lens should equal the
+ * plan's. The kernels use min(device length, plan length): a smaller device length
+ * leaves trailing splits empty (merged correctly), a larger one is cut to the plan's,
+ * so no call reads a block-table entry beyond the ones the plan covers.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1)       /* null pointer, non-positive size, L_b < q_len, ... */
+#define MLA_ERR_UNSUPPORTED_SHAPE (-2) /* outside the limits below */
+#define MLA_ERR_WORKSPACE (-3)         /* workspace NULL, misaligned or too small */
+#define MLA_ERR_NOMEM (-4)             /* host allocation of the plan failed */
+#define MLA_ERR_HIP_BASE (-1000)       /* MLA_ERR_HIP_BASE - hipError_t */
+
+#define MLA_D_QK 576      /* bytes per cached row: latent 512 + rope 64 */
+#define MLA_D_V 512       /* latent width = V width = O width */
+#define MLA_PAGE_SIZE 32  /* tokens per cache page */
+#define MLA_MAX_BATCH 256 /* requests per plan */
+#define MLA_MAX_ROWS_PER_REQUEST 4096 /* q_len * num_heads */
+#define MLA_MAX_SPLIT_KV 1024         /* cap on splits per request */
+
+typedef struct mla_decode_plan_s mla_decode_plan_t;
+
+/*
+ * Build a split plan from the host copy of the KV lengths (the planner of the
+ * per-request split plan in issue #20510, Repro 2, rewritten for 256 CUs).
+ *   kv_lens_host  int32 [batch], each >= q_len
+ *   split_kv > 0  uniform plan: every request gets min(split_kv, max_split_kv,
+ *                 ceil(L_b / 32)) splits (the clamp of the plan to [1, split_kv]
+ *                 described in that issue's follow-up comment);
+ *   split_kv == 0 planner: splits per request in proportion to L_b so that all
+ *                 (split, row block) work items fill num_cus CUs in one wave, capped at
+ *                 max_split_kv (the issue raises that cap to 128 "so that one request
+ *                 can fill the GPU");
+ *   max_split_kv  cap on splits per request, 1 .. MLA_MAX_SPLIT_KV (128 recommended);
+ *   num_cus       compute units to fill; 0 = query the current HIP device.
+ * Every split holds a whole number of pages and none is empty. Splits are issued
+ * longest request first. On success *out owns host memory freed by
+ * mla_decode_plan_destroy.
+ */
+int mla_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
+                    int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
+                    int32_t num_cus, mla_decode_plan_t** out);
+
+void mla_decode_plan_destroy(mla_decode_plan_t* plan);
+
+/* Bytes of workspace the plan needs (fp32 partials: (512 + 4) * 4 bytes per
+ * (row, split)). 0 for a NULL plan. */
+size_t mla_decode_workspace_size(const mla_decode_plan_t* plan);
+
+/* Introspection, for tests and logs. splits/chunk_tokens may be NULL; otherwise they
+ * receive S_b and the split length in tokens (a multiple of 32) per request. */
+typedef struct {
+  int32_t batch, q_len, num_heads;
+  int32_t rows_per_request; /* q_len * num_heads */
+  int32_t row_tiles;        /* row blocks (<= 64 rows each): workgroups per split */
+  int32_t total_splits;     /* sum_b S_b */
+  int32_t work_items;       /* total_splits * row_tiles */
+  int32_t merge_groups;     /* wavefront groups per row in the merge (power of 2) */
+  int32_t max_splits;       /* max_b S_b */
+} mla_decode_plan_info_t;
+
+int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,
+                             int32_t* splits, int32_t* chunk_tokens);
+
+/*
+ * Split-KV partial pass (issue #20510's FP8 split-KV kernel, redesigned for gfx950):
+ * for every (request, split, row block) it gathers the split's pages into LDS with
+ * 16-byte loads, forms QK^T on FP8 MFMA with fp32 accumulation, runs an exp2 online
+ * softmax, and forms PV on FP8 MFMA with V read from the same LDS rows, writing fp32
+ * partials to the workspace. softmax_scale is the fp32 scale on q . k.
+ */
+int mla_decode_partial(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride,
+                       const int32_t* kv_lens, float softmax_scale, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Merge pass (PR #20380's reduction, re-done for wavefronts): combines each row's
+ * partials into O = output_scale * O / l, rounded to BF16 (nearest even), and
+ * LSE = ln sum exp(s_i) in fp32 (skipped when lse is NULL). Empty partials (a split
+ * in which a causal row sees no key) are skipped.
+ */
+int mla_decode_merge(const mla_decode_plan_t* plan, const void* workspace,
+                     size_t workspace_bytes, float output_scale, void* o, float* lse,
+                     void* stream);
+
+/* As mla_decode_merge, but O is written as fp32 [B][q_len][H][512]: the values the
+ * BF16 variant rounds. Used to compare results across split plans before rounding. */
+int mla_decode_merge_f32(const mla_decode_plan_t* plan, const void* workspace,
+                         size_t workspace_bytes, float output_scale, float* o, float* lse,
+                         void* stream);
+
+/* mla_decode_partial followed by mla_decode_merge on the same stream. */
+int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+               const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+               float softmax_scale, float output_scale, void* workspace,
+               size_t workspace_bytes, void* o, float* lse, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mla_decode_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

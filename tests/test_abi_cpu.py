@@ -1,0 +1,152 @@
+"""Host-side checks of libmla_decode.so that need no GPU: the exported symbols match the
+header, the planner's splits, and argument validation (every rejected call returns
+before anything is launched)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+from decode_attention_gather_amd import mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_decode\w*)\s*\(", text)))
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert set(declared) == set(mla.EXPORTS), declared
+    lib = mla.lib_handle()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def plan(lens, q_len=1, heads=12, split=0, cap=128, cus=256):
+    return mla.Plan(lens, q_len=q_len, num_heads=heads, split_kv=split, max_split_kv=cap,
+                    num_cus=cus)
+
+
+@pytest.mark.parametrize("lens,q,h,split,exp_splits,exp_chunk", [
+    ([2048], 1, 12, 4, [4], [512]),
+    ([131072] * 4, 1, 12, 25, [25] * 4, [5248] * 4),
+    ([131072] * 16, 8, 12, 6, [6] * 16, [21856] * 16),
+    ([1048576], 1, 12, 100, [100], [10496]),
+    ([1], 1, 12, 4, [1], [32]),          # one token: one split of one page
+    ([65], 8, 12, 3, [3], [32]),         # last split holds a single token
+    ([100], 1, 12, 0, [4], [32]),        # planner, short: limited by pages
+])
+def test_uniform_and_short_plans(lens, q, h, split, exp_splits, exp_chunk):
+    p = plan(lens, q, h, split)
+    info, splits, chunk = p.info()
+    assert splits == exp_splits and chunk == exp_chunk
+    assert info.rows_per_request == q * h
+    assert info.row_tiles == math.ceil(math.ceil(q * h / 16) / 4)  # blocks of <= 64 rows
+    assert info.total_splits == sum(splits)
+    assert info.work_items == sum(splits) * info.row_tiles
+
+
+def check_cover(lens, splits, chunk):
+    for L, s, c in zip(lens, splits, chunk):
+        assert c % 32 == 0 and c > 0
+        assert (s - 1) * c < L <= s * c, (L, s, c)  # no empty split, full coverage
+
+
+@pytest.mark.parametrize("lens", [[131072] * 16, [131072] * 4, [1048576], [4096, 131072, 70000, 5000],
+                                  [32] * 200, [7, 1000, 123456, 99]])
+def test_planner_one_wave(lens):
+    p = plan(lens, 1, 12, 0, 128, 256)
+    info, splits, chunk = p.info()
+    check_cover(lens, splits, chunk)
+    assert max(splits) <= 128
+    # at most one wave unless every request is already at one split
+    assert info.work_items <= 256 or max(splits) == 1
+    if len(lens) == 16 and len(set(lens)) == 1:
+        assert splits == [16] * 16
+
+
+def test_planner_proportional_and_cap():
+    lens = [4096, 131072, 65536, 8192]
+    p = plan(lens, 1, 12, 0, 128, 256)
+    _, splits, chunk = p.info()
+    check_cover(lens, splits, chunk)
+    assert splits[1] >= splits[2] >= splits[3] >= splits[0]
+    p = plan([1048576], 1, 12, 0, 128, 256)
+    assert p.info()[1] == [128]
+    p = plan([1048576], 1, 12, 0, 256, 256)
+    assert p.info()[1] == [256]
+
+
+def test_merge_groups_rule():
+    assert plan([1048576], 1, 12, 100).info()[0].merge_groups == 16
+    assert plan([2048], 1, 12, 4).info()[0].merge_groups == 4
+    assert plan([131072] * 16, 8, 12, 6).info()[0].merge_groups == 1  # 1536 rows fill the GPU
+    assert plan([100], 1, 12, 1).info()[0].merge_groups == 1
+
+
+def test_workspace_size():
+    p = plan([131072] * 16, 8, 12, 6)
+    assert p.workspace_size() == 96 * 96 * 512 * 4 + 96 * 96 * 4 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=[8], q_len=9), mla.MLA_ERR_INVALID_ARG),          # L < q_len
+    (dict(lens=[8], q_len=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=[8], heads=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=[8], split=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=[8], cap=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=[8], cap=2000), mla.MLA_ERR_UNSUPPORTED_SHAPE),
+    (dict(lens=[8] * 257), mla.MLA_ERR_UNSUPPORTED_SHAPE),
+    (dict(lens=[8], q_len=8, heads=600), mla.MLA_ERR_UNSUPPORTED_SHAPE),
+])
+def test_plan_rejects(kw, status):
+    args = dict(lens=[8], q_len=1, heads=12, split=0, cap=128, cus=256)
+    args.update(kw)
+    with pytest.raises(mla.MlaError) as ei:
+        plan(args["lens"], args["q_len"], args["heads"], args["split"], args["cap"], args["cus"])
+    assert ei.value.status == status
+
+
+def test_call_validation_before_launch():
+    """Bad arguments are rejected on the host; these calls never reach a launch."""
+    lib = mla.lib_handle()
+    p = plan([100, 50], 1, 12, 2)
+    ws_need = p.workspace_size()
+    fake = ctypes.c_void_p(0x10000)  # aligned, never dereferenced on these paths
+    nul = None
+    # null q
+    assert lib.mla_decode_partial(p.handle, nul, fake, fake, 4, fake, 0.07, fake, ws_need,
+                                  nul) == mla.MLA_ERR_INVALID_ARG
+    # block-table row too short for 100 tokens (needs 4 pages)
+    assert lib.mla_decode_partial(p.handle, fake, fake, fake, 3, fake, 0.07, fake, ws_need,
+                                  nul) == mla.MLA_ERR_INVALID_ARG
+    # misaligned q
+    assert lib.mla_decode_partial(p.handle, ctypes.c_void_p(0x10001), fake, fake, 4, fake, 0.07,
+                                  fake, ws_need, nul) == mla.MLA_ERR_INVALID_ARG
+    # non-finite scale
+    assert lib.mla_decode_partial(p.handle, fake, fake, fake, 4, fake, float("nan"), fake,
+                                  ws_need, nul) == mla.MLA_ERR_INVALID_ARG
+    # workspace too small / misaligned / null
+    assert lib.mla_decode_partial(p.handle, fake, fake, fake, 4, fake, 0.07, fake, ws_need - 1,
+                                  nul) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_partial(p.handle, fake, fake, fake, 4, fake, 0.07,
+                                  ctypes.c_void_p(0x10010), ws_need, nul) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_merge(p.handle, nul, ws_need, 1.0, fake, nul, nul) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_merge(p.handle, fake, ws_need, 1.0, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_merge_f32(p.handle, fake, ws_need, float("inf"), fake, nul,
+                                    nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode(None, fake, fake, fake, 4, fake, 0.07, 1.0, fake, ws_need, fake, nul,
+                          nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_workspace_size(None) == 0
+
+
+def test_strerror():
+    for s in (0, -1, -2, -3, -4, -1001, 7):
+        assert isinstance(mla.strerror(s), str) and mla.strerror(s)

@@ -1,0 +1,250 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on seeded inputs.
+
+Bar (element by element):
+  |O_gpu - O_ref| <= 1e-2 + 1e-2 * |O_ref|        (BF16 output)
+  |LSE_gpu - LSE_ref| <= 1e-4 * max(1, |LSE_ref|) (fp32 LSE; relative, with an absolute
+                                                   floor where LSE is near 0)
+Small cases are checked on every row; the full-size workloads, in the launch
+configuration the benchmark times, on sampled rows the oracle computes one by one.
+Inputs carry NaN poison in every cache byte the kernel must not read (see inputs.py),
+so an out-of-range read shows up as a NaN mismatch.
+"""
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_gather_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F32 = lambda x: float(np.float32(x))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    from decode_attention_gather_amd import mla as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def run_gpu(mla, case, split_kv=None, max_split_kv=128, f32_out=False, dc=None):
+    dc = dc or mla.to_device(case)
+    sk = case.split_kv if split_kv is None else split_kv
+    plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads, split_kv=sk,
+                    max_split_kv=max_split_kv)
+    o, lse = mla.run_decode(dc, plan, f32_out=f32_out)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), plan
+
+
+def run_oracle(case, rows=None):
+    return oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=case.q_len,
+                             num_heads=case.num_heads, softmax_scale=F32(case.softmax_scale),
+                             output_scale=F32(case.output_scale), rows=rows)
+
+
+def assert_parity(o, lse, o_ref, lse_ref, tag=""):
+    assert np.isfinite(o).all(), f"{tag}: non-finite O"
+    assert np.isfinite(lse).all(), f"{tag}: non-finite LSE"
+    err = np.abs(o - o_ref)
+    bound = 1e-2 + 1e-2 * np.abs(o_ref)
+    worst = float((err / bound).max())
+    lerr = np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+    _say(f"  {tag}: worst |dO|/bound = {worst:.3f}, max |dLSE| rel = {float(lerr.max()):.2e}")
+    assert (err <= bound).all(), f"{tag}: O mismatch, worst ratio {worst}"
+    assert (lerr <= 1e-4).all(), f"{tag}: LSE mismatch {float(lerr.max())}"
+
+
+SMALL = [
+    # name, kv_lens, heads, q_len, split_kv
+    ("q1_ragged_split3", [1, 100, 2049], 12, 1, 3),
+    ("q8_causal_6tiles", [8, 777], 12, 8, 4),
+    ("q3_h5_rows15", [33, 64, 3], 5, 3, 2),
+    ("q8_last_split_one_token", [65, 97], 12, 8, 3),
+    ("q1_single_split_long", [5000], 12, 1, 1),
+    ("q2_h16_planner", [1500, 40, 2], 16, 2, 0),
+    ("h96_q8_planner", [300, 1000], 96, 8, 0),
+    ("q1_many_requests", [37 * i + 5 for i in range(1, 20)], 12, 1, 0),
+    ("q4_h1_split5", [640, 641], 1, 4, 5),
+    ("odd_pages_split2", [3 * 32 + 7, 5 * 32], 12, 1, 2),
+]
+
+
+@pytest.mark.parametrize("name,lens,heads,q_len,split", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(mla, name, lens, heads, q_len, split):
+    case = inputs.make_case(lens, num_heads=heads, q_len=q_len, seed=zlib.crc32(name.encode()) % 10000,
+                            split_kv=split)
+    _say(f"[gpu] small {name}: lens={lens} H={heads} q={q_len} split={split}")
+    o, lse, _ = run_gpu(mla, case)
+    o_ref, lse_ref = run_oracle(case)
+    assert_parity(o, lse, o_ref, lse_ref, name)
+
+
+def test_output_scale_and_extreme_scores(mla):
+    case = inputs.make_case([300, 129], num_heads=12, q_len=2, seed=5, split_kv=3,
+                            softmax_scale=0.5, output_scale=0.37)
+    _say("[gpu] output_scale 0.37, softmax_scale 0.5")
+    o, lse, _ = run_gpu(mla, case)
+    o_ref, lse_ref = run_oracle(case)
+    assert_parity(o, lse, o_ref, lse_ref, "scales")
+
+
+def test_kv_len_one_and_equal_scores(mla):
+    # one key per request: O is that key's V (exactly representable in BF16)
+    case = inputs.make_case([1, 1, 1], num_heads=12, q_len=1, seed=6, split_kv=1)
+    _say("[gpu] kv_len 1")
+    o, lse, _ = run_gpu(mla, case)
+    o_ref, lse_ref = run_oracle(case)
+    assert np.array_equal(o, o_ref.astype(np.float32)), "kv_len 1 must return V exactly"
+    assert_parity(o, lse, o_ref, lse_ref, "kv_len1")
+    # q = 0: equal scores, O = mean of V
+    case = inputs.make_case([100, 1000], num_heads=12, q_len=1, seed=7, split_kv=4)
+    case.q.zero_()
+    _say("[gpu] equal scores")
+    o, lse, _ = run_gpu(mla, case)
+    o_ref, lse_ref = run_oracle(case)
+    assert_parity(o, lse, o_ref, lse_ref, "equal")
+    np.testing.assert_allclose(lse, np.log([100.0] * 12 + [1000.0] * 12), rtol=1e-6)
+
+
+def test_split_invariance_f32(mla):
+    """fp32 O (before the BF16 cast) from different split plans agrees to 1e-5."""
+    case = inputs.make_case([3000, 20000, 777], num_heads=12, q_len=8, seed=8)
+    dc = mla.to_device(case)
+    outs = []
+    for sk in (1, 2, 5, 0, 13):
+        _say(f"[gpu] split invariance split_kv={sk}")
+        o, lse, plan = run_gpu(mla, case, split_kv=sk, f32_out=True, dc=dc)
+        outs.append((sk, o, lse))
+    base = outs[0]
+    for sk, o, lse in outs[1:]:
+        d = float(np.abs(o - base[1]).max())
+        dl = float(np.abs(lse - base[2]).max())
+        _say(f"  split {sk} vs 1: max |dO| = {d:.3e}, max |dLSE| = {dl:.3e}")
+        assert d <= 1e-5, (sk, d)
+        assert dl <= 1e-5 * max(1.0, float(np.abs(base[2]).max())), (sk, dl)
+
+
+def test_determinism(mla):
+    case = inputs.make_case([4096, 777], num_heads=12, q_len=8, seed=9, split_kv=3)
+    dc = mla.to_device(case)
+    _say("[gpu] determinism")
+    o1, l1, _ = run_gpu(mla, case, dc=dc)
+    o2, l2, _ = run_gpu(mla, case, dc=dc)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_device_lengths_shorter_than_plan(mla):
+    """A device kv_len below the planned one leaves trailing splits empty; the result is
+    the one for the shorter length."""
+    case = inputs.make_case([640], num_heads=12, q_len=1, seed=10, split_kv=5)
+    dc = mla.to_device(case)
+    plan = mla.Plan([640], q_len=1, num_heads=12, split_kv=5)  # 5 splits of 4 pages
+    dc.kv_lens.fill_(200)  # splits 2..4 become empty
+    _say("[gpu] device lengths shorter than plan")
+    o, lse = mla.run_decode(dc, plan)
+    torch.cuda.synchronize()
+    short = inputs.Case(q=case.q, kv=case.kv, block_table=case.block_table,
+                        kv_lens=torch.tensor([200], dtype=torch.int32), q_len=1, num_heads=12)
+    o_ref, lse_ref = run_oracle(short)
+    assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "short-device")
+
+
+# ---- merge kernel alone, on synthetic partials -------------------------------------
+
+def _merge_reference(m, l, lt, O, S_list, out_scale):
+    """fp64 combine of (m, l, l~, O) partials [parts, rows, ...] per request."""
+    rows = m.shape[1]
+    outs, lses = [], []
+    base = 0
+    for S in S_list:
+        mm = m[base:base + S].astype(np.float64)
+        M = np.max(mm, axis=0)
+        w = np.where(np.isneginf(mm), 0.0, np.exp2(mm - M))
+        Ls = (w * l[base:base + S]).sum(0)
+        Lt = (w * lt[base:base + S]).sum(0)
+        Osum = (w[:, :, None] * O[base:base + S]).sum(0)
+        outs.append(out_scale * Osum / Lt[:, None])
+        lses.append(math.log(2.0) * (M - 8.0 + np.log2(Ls)))
+        base += S
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+@pytest.mark.parametrize("lens,split,heads,q_len", [([1048576], 100, 12, 1), ([2048], 4, 12, 1),
+                                                    ([131072] * 4, 25, 12, 1), ([5000, 90], 7, 3, 2)])
+def test_merge_synthetic(mla, lens, split, heads, q_len):
+    plan = mla.Plan(lens, q_len=q_len, num_heads=heads, split_kv=split)
+    info, splits, _ = plan.info()
+    rows = info.rows_per_request
+    parts = info.total_splits
+    g = torch.Generator().manual_seed(123)
+    m = torch.randint(-20, 21, (parts, rows), generator=g).double().numpy()
+    empty = torch.rand((parts, rows), generator=g).numpy() < 0.15
+    m[empty] = -np.inf
+    l = (torch.rand((parts, rows), generator=g).double().numpy() * 300.0 + 1.0)
+    lt = l * (1.0 + 1e-3 * torch.randn((parts, rows), generator=g).double().numpy())
+    O = torch.randn((parts, rows, 512), generator=g).double().numpy() * l[:, :, None] * 0.1
+    l[empty] = 0.0
+    lt[empty] = 0.0
+    O[empty] = 0.0
+    base = 0
+    for S in splits:  # force one live partial per row of each request
+        m[base, :] = np.where(np.isneginf(m[base, :]), 3.0, m[base, :])
+        l[base, :] = np.where(l[base, :] == 0.0, 5.0, l[base, :])
+        lt[base, :] = np.where(lt[base, :] == 0.0, 5.0, lt[base, :])
+        base += S
+    ws = plan.alloc_workspace()
+    o_bytes = parts * rows * 512 * 4
+    ws_o = ws[:o_bytes].view(torch.float32)
+    ws_st = ws[o_bytes:o_bytes + parts * rows * 16].view(torch.float32)
+    ws_o.copy_(torch.from_numpy(O.astype(np.float32).reshape(-1)))
+    st = np.stack([m, l, lt, np.zeros_like(l)], axis=-1).astype(np.float32)
+    ws_st.copy_(torch.from_numpy(st.reshape(-1)))
+    # the reference takes the same fp32 values the kernel sees
+    O32 = O.astype(np.float32).astype(np.float64)
+    ref_o, ref_lse = _merge_reference(st[..., 0], st[..., 1].astype(np.float64),
+                                      st[..., 2].astype(np.float64), O32, splits, 0.5)
+    o = torch.empty((len(lens) * rows, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((len(lens) * rows,), dtype=torch.float32, device="cuda")
+    _say(f"[gpu] merge synthetic lens={lens} split={split} groups={info.merge_groups}")
+    mla.merge(plan, ws, 0.5, o, lse)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o.cpu().numpy(), ref_o, rtol=2e-5, atol=1e-6)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, rtol=1e-5, atol=1e-5)
+    ob = torch.empty((len(lens) * rows, 512), dtype=torch.bfloat16, device="cuda")
+    mla.merge(plan, ws, 0.5, ob, None)
+    torch.cuda.synchronize()
+    # BF16 output is the RNE rounding of the fp32 result
+    assert torch.equal(ob.cpu(), o.cpu().to(torch.bfloat16))
+
+
+# ---- full-size workloads (launch configuration of the benchmark), sampled rows --------
+
+FULL = ["c1_b1_h12_q1_2k", "c2_b4_h12_q1_128k", "c3_b16_h12_q8_128k", "c4_b1_h12_q1_1m",
+        "c5_b8_h96_q8_mixed", "m_b16_h12_q1_128k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config_sampled(mla, name):
+    _say(f"[gpu] full config {name}: generating inputs")
+    case = inputs.make_config(name)
+    rows = inputs.sample_rows(case, 24)
+    dc = mla.to_device(case)
+    for sk in ([case.split_kv, 0] if case.split_kv else [0]):
+        _say(f"[gpu] full config {name}: split_kv={sk}")
+        o, lse, plan = run_gpu(mla, case, split_kv=sk, dc=dc)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        o_ref, lse_ref = run_oracle(case, rows)
+        assert_parity(o[rows], lse[rows], o_ref, lse_ref, f"{name} split={sk}")
+    del dc
+    torch.cuda.empty_cache()
