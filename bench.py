@@ -47,21 +47,48 @@ def algorithmic_bytes(case) -> dict:
     return dict(kv=kv, q=q, bt=bt, out=out, partial_in=kv + q + bt, total=kv + q + bt + out)
 
 
-def time_calls(fn, steps, warmup, stream):
+def profiled_traffic(config: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter summary
+    (profiles/partial_kernel_<config>.md), or None when the kernel source changed since
+    the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"partial_kernel_{config}.md")
+    src = os.path.join(ROOT, "decode_attention_gather_amd", "csrc", "partial.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        k, sep, v = line.strip().partition(": ")
+        if sep and k in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            fields[k] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def time_calls(fn, steps, warmup, stream, reps=1):
+    """`warmup` untimed calls, then `reps` timed runs of exactly `steps` back-to-back calls,
+    each bracketed by torch.cuda.synchronize() and one pair of HIP events on `stream`.
+    Returns the per-run time per call (us) and the host wall time of the last run."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
+    per = []
+    wall = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         a.record(stream)
-        fn()
+        for _ in range(steps):
+            fn()
         b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])  # us
-    return per, wall
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per.append(a.elapsed_time(b) * 1e3 / steps)
+    return np.array(per), wall
 
 
 def bench_config(mla, name, split_kv, steps, warmup, dc=None, case=None):
@@ -93,8 +120,8 @@ def bench_config(mla, name, split_kv, steps, warmup, dc=None, case=None):
     return dict(
         config=name, split_kv=split_kv, splits=sorted(set(splits)), work_items=info.work_items,
         merge_groups=info.merge_groups, plan_us=round(plan_us, 1),
-        us_per_call=round(us, 2), us_p10=round(float(np.percentile(per_call, 10)), 2),
-        us_p90=round(float(np.percentile(per_call, 90)), 2),
+        us_per_call=round(us, 2), us_min=round(float(per_call.min()), 2),
+        us_max=round(float(per_call.max()), 2),
         kv_gbs=round(by["kv"] / (us * 1e-6) / 1e9, 1),
         partial_us=round(us_p, 2), partial_gbs=round(by["partial_in"] / (us_p * 1e-6) / 1e9, 1),
         merge_us=round(us - us_p, 2), wall_s=round(wall, 4), bytes=by, case=case, dc=dc)
@@ -104,8 +131,7 @@ def cpu_baseline(case, budget_rows=None):
     """The fp64 oracle on a bounded sample of the workload's rows (all host cores)."""
     import oracle
     threads = oracle.hw_threads()
-    nrows = budget_rows or max(threads, 8)
-    nrows = min(nrows, case.rows)
+    nrows = min(budget_rows or case.rows, case.rows)
     rows = inputs.sample_rows(case, nrows)
     t0 = time.perf_counter()
     oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=case.q_len,
@@ -127,6 +153,9 @@ def main():
     ap.add_argument("--config", default=HEADLINE, choices=sorted(inputs.CONFIGS))
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--planner-only", action="store_true", help="skip the fixed-split plan")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,6 +166,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": x.numel() * 4, "copies": 3}))
+        return
     from decode_attention_gather_amd import mla
 
     name = args.config
@@ -146,7 +183,7 @@ def main():
     native = bench_config(mla, name, 0, args.steps, args.warmup, dc=dc, case=case)
     print(f"[bench] planner plan: {native['us_per_call']} us/call", file=sys.stderr, flush=True)
     fixed = None
-    if case.split_kv:
+    if case.split_kv and not args.planner_only:
         fixed = bench_config(mla, name, case.split_kv, args.steps, args.warmup, dc=dc, case=case)
         print(f"[bench] split_kv={case.split_kv}: {fixed['us_per_call']} us/call", file=sys.stderr,
               flush=True)
@@ -180,7 +217,7 @@ def main():
             "work_items": fixed["work_items"]},
         "roofline": {"bound": "hbm", "kernel": "partial_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
                      "bytes_per_launch": by["partial_in"], "us_per_launch": native["partial_us"]},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample",
