@@ -19,7 +19,7 @@ constexpr int kDV = MLA_D_V;               // 512 latent = V = O width
 constexpr int kPage = MLA_PAGE_SIZE;       // 32 tokens per page
 constexpr int kPageBytes = kPage * kDQK;   // 18432
 constexpr int kTileRows = 16;              // query rows per MFMA row tile
-constexpr int kMaxTilesPerBlock = 4;      // row tiles per workgroup (64 rows)
+constexpr int kMaxTilesPerBlock = 2;      // row tiles per workgroup (32 rows)
 constexpr int kMaxBatch = MLA_MAX_BATCH;
 constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)

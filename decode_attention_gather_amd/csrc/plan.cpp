@@ -67,7 +67,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   }
 
   const int32_t rows = q_len * num_heads;
-  // Row blocks: at most 4 MFMA row tiles (64 rows) per workgroup, balanced, so that one
+  // Row blocks: at most 2 MFMA row tiles (32 rows) per workgroup, balanced, so that one
   // staged page feeds as many rows as the workgroup's registers hold.
   const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
   const int32_t tiles = (int32_t)ceil_div(tiles16, kMaxTilesPerBlock);

@@ -48,7 +48,7 @@ def test_uniform_and_short_plans(lens, q, h, split, exp_splits, exp_chunk):
     info, splits, chunk = p.info()
     assert splits == exp_splits and chunk == exp_chunk
     assert info.rows_per_request == q * h
-    assert info.row_tiles == math.ceil(math.ceil(q * h / 16) / 4)  # blocks of <= 64 rows
+    assert info.row_tiles == math.ceil(math.ceil(q * h / 16) / 2)  # blocks of <= 32 rows
     assert info.total_splits == sum(splits)
     assert info.work_items == sum(splits) * info.row_tiles
 
