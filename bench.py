@@ -2,14 +2,18 @@
 """Benchmark of split-KV MLA decode (partial + merge) on one MI355X.
 
 A step is one mla_decode call (split-KV partial kernel + merge kernel) over one batch of
-synthetic, HBM-resident inputs; the host plan is built once, outside the timed region,
-and its cost is reported separately. The headline workload is H12 q1 B16 128K
-(16 requests x 131072 tokens, 12 heads, one query token), the metric's shape; `value`
-is the achieved KV-read bandwidth (KV bytes read once per call / time per call) with
-the native one-wave split plan, and the pages' fixed split_kv = 6 plan is reported next
-to it. `roofline` covers the dominant kernel (the split-KV partial kernel), timed with
-HIP events on the stream it is launched on; `cpu_baseline` is the fp64 oracle on a
-bounded sample of the same workload.
+synthetic, HBM-resident inputs; host plans are built once, outside the timed region,
+and their cost is reported separately. The headline workload is H12 q1 B16 128K
+(16 requests x 131072 tokens, 12 heads, one query token). `value` is the achieved
+KV-read bandwidth (KV bytes read once per call / time per call) with the native
+one-wave split plan; the pages' fixed split_kv = 6 plan is timed first (it also brings
+the GPU clocks up from idle) and reported beside it, and the q = 8 sibling of the
+workload (same KV, 8 causal query tokens) is reported as `q8`.
+
+`roofline` covers the dominant kernel (the split-KV partial kernel), timed with HIP
+events on the stream it is launched on; `cpu_baseline` is the fp64 oracle on a bounded
+sample of the same workload. Per-call times come from one event between consecutive
+calls (median, p10, p90); `ms_per_step` is the whole timed region divided by the steps.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--all]
 """
@@ -30,14 +34,16 @@ sys.path.insert(0, ROOT)
 from decode_attention_gather_amd import inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA peak of the MI355X
+FLOP_PER_ROW_TOKEN = 2 * (576 + 512)  # QK^T over 576 dims + PV over 512 dims
 METRIC = "µs per MLA decode call + achieved KV-read HBM GB/s (H12 q1 B16 128K)"
 HEADLINE = "m_b16_h12_q1_128k"
+COLD_BYTES = 512 << 20          # written between calls to evict the 256 MB MALL
 
 
 def algorithmic_bytes(case) -> dict:
     """Bytes the method must move once: every visible token's 576-byte cache row, the
     query rows, the block-table entries, and the outputs (BF16 O + fp32 LSE)."""
-    B = case.batch
     rows = case.rows
     pages = int(sum((int(L) + 31) // 32 for L in case.kv_lens.tolist()))
     kv = case.kv_bytes
@@ -45,6 +51,12 @@ def algorithmic_bytes(case) -> dict:
     bt = pages * 4
     out = rows * (512 * 2 + 4)
     return dict(kv=kv, q=q, bt=bt, out=out, partial_in=kv + q + bt, total=kv + q + bt + out)
+
+
+def algorithmic_flops(kv_lens, q_len, num_heads) -> int:
+    """2176 flop per (row, visible token); query j of q sees L - q + j + 1 tokens."""
+    tok = sum(int(L) - q_len + j + 1 for L in kv_lens for j in range(q_len))
+    return tok * num_heads * FLOP_PER_ROW_TOKEN
 
 
 def profiled_traffic(config: str):
@@ -67,64 +79,138 @@ def profiled_traffic(config: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def time_calls(fn, steps, warmup, stream, reps=1):
-    """`warmup` untimed calls, then `reps` timed runs of exactly `steps` back-to-back calls,
-    each bracketed by torch.cuda.synchronize() and one pair of HIP events on `stream`.
-    Returns the per-run time per call (us) and the host wall time of the last run."""
+def time_steps(fn, steps, warmup, stream):
+    """`warmup` untimed calls, then exactly `steps` back-to-back calls bracketed by
+    torch.cuda.synchronize(), with a HIP event on `stream` before the first call and
+    after every call. Returns (total µs / steps, per-call µs array, host wall s)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    per = []
-    wall = 0.0
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+    return ev[0].elapsed_time(ev[steps]) * 1e3 / steps, per, wall
+
+
+def time_cold(fn, calls, stream):
+    """Per-call µs with the MALL (and L2) evicted before each call: a 512 MB buffer is
+    written between calls, outside the event pair."""
+    scratch = torch.empty(COLD_BYTES, dtype=torch.uint8, device="cuda")
+    fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(calls):
+        scratch.fill_(1)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         a.record(stream)
-        for _ in range(steps):
-            fn()
+        fn()
         b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per.append(a.elapsed_time(b) * 1e3 / steps)
-    return np.array(per), wall
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    del scratch
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
 
 
-def bench_config(mla, name, split_kv, steps, warmup, dc=None, case=None):
-    case = case if case is not None else inputs.make_config(name)
-    dc = dc if dc is not None else mla.to_device(case)
+def stats(per):
+    return dict(median=round(float(np.median(per)), 2), p10=round(float(np.percentile(per, 10)), 2),
+                p90=round(float(np.percentile(per, 90)), 2))
+
+
+def bench_plan(mla, dc, q, rows, kv_bytes, kv_lens, split_kv, steps, warmup, cold_calls=0):
+    """Times mla_decode calls and partial-only launches of one plan."""
     t0 = time.perf_counter()
-    plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads,
-                    split_kv=split_kv, max_split_kv=128)
+    plan = mla.Plan(kv_lens, q_len=q.shape[1], num_heads=q.shape[2], split_kv=split_kv,
+                    max_split_kv=128)
     plan_us = (time.perf_counter() - t0) * 1e6
-    info, splits, chunk = plan.info()
+    info, splits, _ = plan.info()
     ws = plan.alloc_workspace()
-    rows = case.rows
     o = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def call():
-        mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+        mla.decode(plan, q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
                    dc.output_scale, ws, o, lse, stream)
 
     def partial_only():
-        mla.partial(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale, ws, stream)
+        mla.partial(plan, q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale, ws, stream)
 
-    per_call, wall = time_calls(call, steps, warmup, stream)
-    per_partial, _ = time_calls(partial_only, steps, warmup, stream)
-    by = algorithmic_bytes(case)
-    us = float(np.median(per_call))
-    us_p = float(np.median(per_partial))
-    return dict(
-        config=name, split_kv=split_kv, splits=sorted(set(splits)), work_items=info.work_items,
-        merge_groups=info.merge_groups, plan_us=round(plan_us, 1),
-        us_per_call=round(us, 2), us_min=round(float(per_call.min()), 2),
-        us_max=round(float(per_call.max()), 2),
-        kv_gbs=round(by["kv"] / (us * 1e-6) / 1e9, 1),
-        partial_us=round(us_p, 2), partial_gbs=round(by["partial_in"] / (us_p * 1e-6) / 1e9, 1),
-        merge_us=round(us - us_p, 2), wall_s=round(wall, 4), bytes=by, case=case, dc=dc)
+    us, per, wall = time_steps(call, steps, warmup, stream)
+    us_p, per_p, _ = time_steps(partial_only, steps, warmup, stream)
+    res = dict(split_kv=split_kv, splits=sorted(set(splits)), work_items=info.work_items,
+               row_tiles=info.row_tiles, merge_groups=info.merge_groups,
+               plan_us=round(plan_us, 1), us_per_call=round(us, 2), call=stats(per),
+               kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1),
+               partial_us=round(us_p, 2), partial=stats(per_p),
+               partial_kv_gbs=round(kv_bytes / (us_p * 1e-6) / 1e9, 1),
+               merge_us=round(us - us_p, 2), wall_s=round(wall, 4))
+    if cold_calls:
+        res["cold_mall"] = stats(time_cold(call, cold_calls, stream))
+    plan.close()
+    return res
+
+
+def q8_sibling(case, q_len=8, seed=20263):
+    """Queries for the q = 8 sibling of a workload: N(0, 1) E4M3 rows drawn from their
+    own seeded generator, used with the workload's KV cache and block table."""
+    g = torch.Generator().manual_seed(seed)
+    return inputs.to_e4m3_codes(torch.randn(case.batch, q_len, case.num_heads, 576, generator=g))
+
+
+def graph_timing(mla, dc, case, calls=100, reps=5):
+    """Launch-bound check: `calls` mla_decode calls captured in one HIP graph, replayed,
+    against a graph of 2 * `calls` one-element kernels (the launch floor)."""
+    plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads, split_kv=0)
+    ws = plan.alloc_workspace()
+    o = torch.empty((case.rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case.rows,), dtype=torch.float32, device="cuda")
+    mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+               dc.output_scale, ws, o, lse)
+    torch.cuda.synchronize()
+    o_eager = o.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+                           dc.output_scale, ws, o, lse, s)
+    x = torch.zeros(1, device="cuda")
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(gf, stream=s):
+            for _ in range(2 * calls):
+                x.add_(1.0)
+    torch.cuda.synchronize()
+
+    def replay(gr):
+        gr.replay()
+        torch.cuda.synchronize()
+        best = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            best.append(a.elapsed_time(b) * 1e3 / calls)
+        return float(np.median(best))
+
+    us = replay(g)
+    same = bool(torch.equal(o, o_eager))
+    floor = replay(gf)
+    plan.close()
+    return dict(calls_per_graph=calls, us_per_call=round(us, 2),
+                floor_us_per_2_kernels=round(floor, 2), graph_matches_eager=same)
 
 
 def cpu_baseline(case, budget_rows=None):
@@ -145,14 +231,35 @@ def cpu_baseline(case, budget_rows=None):
                        f"{dt:.2f} s on {threads} threads, scaled to the full call")
 
 
+def bench_other(mla, name, steps, warmup):
+    """Every plan of one more workload (stderr report and the JSON's `all` list)."""
+    c = inputs.make_config(name)
+    dc = mla.to_device(c)
+    by = algorithmic_bytes(c)
+    flops = algorithmic_flops(dc.kv_lens_host, c.q_len, c.num_heads)
+    out = []
+    for sk in ([c.split_kv, 0] if c.split_kv else [0]):
+        r = bench_plan(mla, dc, dc.q, c.rows, by["kv"], dc.kv_lens_host, sk, steps, warmup,
+                       cold_calls=10)
+        r["config"] = name
+        r["mfma_util"] = round(flops / (r["us_per_call"] * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)
+        out.append(r)
+    if name.startswith("c1_"):
+        out[-1]["graph"] = graph_timing(mla, dc, c)
+    del dc
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=HEADLINE, choices=sorted(inputs.CONFIGS))
-    ap.add_argument("--all", action="store_true", help="also time every workload (stderr)")
+    ap.add_argument("--all", action="store_true", help="also time every other workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-q8", action="store_true", help="skip the q = 8 sibling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--planner-only", action="store_true", help="skip the fixed-split plan")
@@ -180,24 +287,52 @@ def main():
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     case = inputs.make_config(name)
     dc = mla.to_device(case)
-    native = bench_config(mla, name, 0, args.steps, args.warmup, dc=dc, case=case)
-    print(f"[bench] planner plan: {native['us_per_call']} us/call", file=sys.stderr, flush=True)
+    by = algorithmic_bytes(case)
+    steps, warmup = args.steps, args.warmup
+
     fixed = None
     if case.split_kv and not args.planner_only:
-        fixed = bench_config(mla, name, case.split_kv, args.steps, args.warmup, dc=dc, case=case)
-        print(f"[bench] split_kv={case.split_kv}: {fixed['us_per_call']} us/call", file=sys.stderr,
-              flush=True)
+        fixed = bench_plan(mla, dc, dc.q, case.rows, by["kv"], dc.kv_lens_host, case.split_kv,
+                           steps, warmup)
+        print(f"[bench] split_kv={case.split_kv}: {fixed['us_per_call']} us/call",
+              file=sys.stderr, flush=True)
+    native = bench_plan(mla, dc, dc.q, case.rows, by["kv"], dc.kv_lens_host, 0, steps, warmup,
+                        cold_calls=20)
+    print(f"[bench] planner plan: {native['us_per_call']} us/call", file=sys.stderr, flush=True)
+
+    q8 = None
+    if not args.no_q8 and name == HEADLINE:
+        q8d = q8_sibling(case).to("cuda")
+        rows8 = q8d.shape[0] * q8d.shape[1] * q8d.shape[2]
+        flops8 = algorithmic_flops(dc.kv_lens_host, 8, case.num_heads)
+        q8 = {"workload": "H12 q8 B16 128K (the headline's KV, 8 causal query tokens)"}
+        for key, sk in (("fixed_split", case.split_kv), ("planner", 0)):
+            r = bench_plan(mla, dc, q8d, rows8, by["kv"], dc.kv_lens_host, sk, steps, warmup)
+            r["mfma_util"] = round(flops8 / (r["us_per_call"] * 1e-6) / 1e12
+                                   / FP8_MFMA_PEAK_TFLOPS, 4)
+            q8[key] = r
+            print(f"[bench] q8 {key}: {r['us_per_call']} us/call", file=sys.stderr, flush=True)
+        del q8d
+
+    others = []
+    if args.all:
+        for other in sorted(inputs.CONFIGS):
+            if other == name:
+                continue
+            for r in bench_other(mla, other, steps, warmup):
+                print("[bench-all] " + json.dumps(r), file=sys.stderr, flush=True)
+                others.append(r)
+
     cpu = None if args.no_cpu else cpu_baseline(case)
 
-    by = native["bytes"]
     achieved = by["partial_in"] / (native["partial_us"] * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": native["kv_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(native["us_per_call"] / 1e3, 5),
         "us_per_call": native["us_per_call"],
         "higher_is_better": True,
@@ -209,12 +344,14 @@ def main():
                    "heads": case.num_heads, "q_len": case.q_len, "page": 32,
                    "split_plan": "planner (one wave, cap 128)", "splits": native["splits"],
                    "work_items": native["work_items"], "parallelism": "1 GPU"},
+        "call": native["call"],
+        "cold_mall": native.get("cold_mall"),
         "plan_us": native["plan_us"],
         "merge_us": native["merge_us"],
         "fixed_split": None if fixed is None else {
-            "split_kv": fixed["split_kv"], "us_per_call": fixed["us_per_call"],
-            "kv_gbs": fixed["kv_gbs"], "partial_us": fixed["partial_us"],
-            "work_items": fixed["work_items"]},
+            k: fixed[k] for k in ("split_kv", "us_per_call", "call", "kv_gbs", "partial_us",
+                                  "work_items")},
+        "q8": q8,
         "roofline": {"bound": "hbm", "kernel": "partial_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
@@ -223,18 +360,8 @@ def main():
                                                   ("value", "unit", "cores", "kind", "sample",
                                                    "us_per_call")},
     }
-    if args.all:
-        for other in sorted(inputs.CONFIGS):
-            if other == name:
-                continue
-            c = inputs.make_config(other)
-            for sk in ([0, c.split_kv] if c.split_kv else [0]):
-                r = bench_config(mla, other, sk, args.steps, args.warmup, case=c)
-                print("[bench-all] " + json.dumps({k: v for k, v in r.items()
-                                                   if k not in ("case", "dc", "bytes")}),
-                      file=sys.stderr, flush=True)
-                del r
-            torch.cuda.empty_cache()
+    if others:
+        res["all"] = others
     print(json.dumps(res), flush=True)
 
 

@@ -110,6 +110,7 @@ class Plan:
         _check(_lib.mla_decode_plan(lens, len(kv_lens), q_len, num_heads, split_kv, max_split_kv,
                                     num_cus, ctypes.byref(h)), "mla_decode_plan")
         self._h = h
+        self._destroy = _lib.mla_decode_plan_destroy  # kept: module globals may be gone at exit
         self.batch = len(kv_lens)
         self.q_len = q_len
         self.num_heads = num_heads
@@ -120,7 +121,7 @@ class Plan:
 
     def close(self):
         if getattr(self, "_h", None):
-            _lib.mla_decode_plan_destroy(self._h)
+            self._destroy(self._h)
             self._h = None
 
     def __del__(self):
