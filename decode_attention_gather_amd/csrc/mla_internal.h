@@ -19,7 +19,8 @@ constexpr int kDV = MLA_D_V;               // 512 latent = V = O width
 constexpr int kPage = MLA_PAGE_SIZE;       // 32 tokens per page
 constexpr int kPageBytes = kPage * kDQK;   // 18432
 constexpr int kTileRows = 16;              // query rows per MFMA row tile
-constexpr int kMaxTilesPerBlock = 2;      // row tiles per workgroup (32 rows)
+constexpr int kMaxTilesPerBlock = 2;       // narrow kernel: row tiles per workgroup
+constexpr int kWideMaxTiles = 6;           // wide kernel: 4 or 6 row tiles (96 rows)
 constexpr int kMaxBatch = MLA_MAX_BATCH;
 constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
@@ -37,7 +38,7 @@ struct PlanDev {
   int32_t rows;         // q_len * heads, rows per request
   int32_t tiles;        // row blocks (workgroups) per split: ceil(rows / (16 nt))
   int32_t total_parts;  // sum of splits
-  int32_t nt;           // 16-row tiles per row block, 1..4
+  int32_t nt;           // 16-row tiles per row block: 1, 2 (narrow) or 4, 6 (wide)
   int32_t pad1;
   uint32_t sorted[kMaxBatch];     // (part_end << 8) | request
   uint32_t kv_len[kMaxBatch];     // per request: the plan's (host) length
@@ -73,6 +74,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream);
+int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                        const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                        float softmax_scale, float* ws_o, float* ws_stats, void* stream);
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream);
 

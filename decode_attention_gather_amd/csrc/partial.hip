@@ -498,6 +498,9 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream) {
   const PlanDev& P = plan.dev;
+  if (P.nt > kMaxTilesPerBlock)
+    return launch_partial_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
+                               stream);
   const int slots = (P.total_parts + 7) / 8;
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;

@@ -1,0 +1,539 @@
+// Split-KV partial kernel for MLA decode, wide row blocks (64 or 96 query rows), gfx950.
+//
+// Computes exactly what the narrow kernel (partial.hip) computes, per (request b,
+// split s, block of 16 NT query rows): the online-softmax state of TensorRT-LLM PR
+// #20380 "trtllm-gen FMHA: split the KV partials of a row across thread groups in
+// fmhaReductionKernel" (Description: per-row max, sum and unnormalised O) over the
+// split's keys, with the causal limit of the MTP verify shape (issue #20510 "CuTe DSL
+// FP8 MLA decode slower after #19338", Setup) and the same P~ quantisation, so the
+// partials are bit-compatible with the narrow kernel's and with every split plan.
+//
+// Why a second kernel: with q = 8 (and with 96 heads) a request has 96-768 rows. The
+// narrow kernel stages the KV through LDS once per 32 rows; here one staged page
+// feeds 64 or 96 rows, so each KV byte crosses HBM->L2->LDS once per 96 rows and the
+// MFMA units, not the gather, set the pace (these shapes need ~300 flop per KV byte).
+//
+// Design for gfx950: one workgroup of NT/2 + 8 wavefronts per work item.
+//  * Gather: direct-to-LDS loads (global_load_lds_dwordx4, 1 KB of one page per
+//    instruction) into a 3-stage ring of 2-page steps, issued by the QK waves two steps
+//    ahead. Rows stay 576 bytes (the load writes LDS contiguously); instead, 16-byte
+//    chunk c of token row n sits at chunk (c + ((n >> 2) & 3)) mod 36, which puts the
+//    16 rows of an operand read, and the 16 consecutive rows of a transposed V read, on
+//    distinct LDS banks. VGPR staging would need ~290 VGPRs per step that the MFMA
+//    waves use for operands and accumulators.
+//  * QK^T: QK wave q owns row tiles 2q and 2q + 1 (Q^T of both in VGPRs) and computes
+//    S^T = K Q^T for both pages of the step with v_mfma_scale_f32_16x16x128_f8f6f4;
+//    every K fragment read from LDS feeds two MFMAs. Softmax as in the narrow kernel:
+//    per (row, page) c = ceil(max t), x = 2^(t - c + 8), P~ = hi + lo / 16.
+//    The QK waves also keep each row's running maximum m (an integer), l = sum x and
+//    l~ = sum P~ (summed from the decoded E4M3 bytes), and publish per step the rescale
+//    factor 2^(m_old - m_new) and the page exponents c_page - m_new.
+//  * PV: 8 waves; wave (group gq, quarter dq) accumulates O for row tiles
+//    [gq NT/2, (gq + 1) NT/2) and dims [128 dq, 128 dq + 128): every transposed V read
+//    feeds NT/2 MFMAs. The page exponents enter through the E8M0 block scales.
+//  * Token order inside an MFMA K block: position 16 G + j of a step (G = lane group)
+//    holds token 32 (G >> 1) + 16 (j >> 3) + 8 (G & 1) + (j & 7), so the 32 lanes that
+//    one transposed read serves at a time read 16 consecutive token rows.
+//  * Skewed single-barrier pipeline: iteration s runs QK/softmax of step s + 1 and PV of
+//    step s; P~ and the page maxima are double-buffered.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kStepPages = 2;
+constexpr int kStepBytes = kStepPages * kPageBytes;  // 36864
+constexpr int kStages = 3;
+constexpr int kChunks = kDQK / 16;                   // 36 chunks of 16 bytes per row
+constexpr int kStepLoads = kStepBytes / 1024;        // 36 wave-wide 16-byte loads per step
+constexpr int kPageLoads = kPageBytes / 1024;        // 18 of them per page
+static_assert(kStepLoads * 1024 == kStepBytes && kPageBytes % 1024 == 0, "1 KB loads tile a step");
+constexpr int kPRow = 144;                           // P~ row: 64 hi, 64 lo, 16 pad
+
+template <int NT>
+struct WRoles {
+  static_assert(NT == 4 || NT == 6, "wide row blocks hold 4 or 6 row tiles");
+  static constexpr int kQKW = NT / 2;                 // QK waves, two row tiles each
+  static constexpr int kPVW = 8;                      // PV waves
+  static constexpr int kWaves = kQKW + kPVW;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRTg = NT / 2;                 // row tiles per PV group
+  static constexpr int kDMA = kStepLoads / kQKW;      // 1 KB loads per QK wave per step
+  static_assert(kDMA * kQKW == kStepLoads && kDMA % 2 == 0, "even share of the step");
+};
+
+template <int NT>
+struct __attribute__((aligned(16))) WSmem {
+  uint8_t pages[kStages][kStepBytes];
+  uint8_t ptile[2][NT * kTileRows * kPRow];
+  float alpha[2][NT * kTileRows];              // per row: 2^(m_old - m_new) of the step
+  float2 sc[2][NT * kTileRows];                // per row: c_page - m_new of both pages
+};
+
+__device__ __forceinline__ int rot_of(int n) { return (n >> 2) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier ordering LDS traffic only (the direct-to-LDS loads still in flight
+// for later stages are awaited explicitly by the waves that issued them).
+__device__ __forceinline__ void block_sync_lds() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One wave-wide direct-to-LDS load: lane i's 16 bytes at sbase + voff land at LDS
+// byte address lds_base + 16 i. Issued from inline asm so that the compiler's
+// wait-count pass does not drain it at every LDS access; M0 carries the LDS base and is
+// restored. The s_nop covers the wait states a vector memory instruction needs after a
+// VALU write of an SGPR it reads (the base may come from v_readfirstlane), which the
+// compiler does not insert in front of inline assembly.
+__device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(base)
+      : "memory");
+}
+
+// A wave-uniform 64-bit address in SGPRs (both halves zero-extended).
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+__device__ __forceinline__ v4i ld16(const uint8_t* base, int off) {
+  return *(const v4i*)(base + off);
+}
+
+__device__ __forceinline__ v8i cat8(v4i a, v4i b) {
+  return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
+// 2^(a - b) for integer-valued a <= b; 0 when a is -inf.
+__device__ __forceinline__ float pow2_diff(float a, float b) {
+  return a == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(a - b));
+}
+
+// Flat workgroup id -> (sorted split index, row block): the row blocks of one split
+// run on one XCD (workgroup i goes to XCD i mod 8), splits dealt round-robin.
+__device__ __forceinline__ bool wg_item(const PlanDev& P, int wg, int* part_sorted, int* blk) {
+  const int x = wg & 7, k = wg >> 3;
+  const int slot = k / P.tiles;
+  *blk = k - slot * P.tiles;
+  *part_sorted = slot * 8 + x;
+  return *part_sorted < P.total_parts;
+}
+
+struct WItem {
+  const PlanDev* P;
+  const uint8_t* q;
+  const uint8_t* kv;
+  const int32_t* btb;
+  float* ws_o;
+  float* ws_stats;
+  float scale_log2;
+  int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int lane, w, g, l16;
+};
+
+// ------------------------------------------------------------------ QK waves
+// QK wave qw: S^T = K Q^T of both pages of a step for row tiles 2 qw and 2 qw + 1, the
+// per-page softmax (P~ to LDS), and the row bookkeeping: running max m (integer), l and
+// l~, with the step's rescale factor 2^(m_old - m_new) and the block-scale exponents
+// c_page - m_new published for the PV waves. Writes the rows' (m, l, l~) at the end.
+template <int NT>
+__device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
+  using R = WRoles<NT>;
+  const PlanDev& P = *it.P;
+  const int lane = it.lane, g = it.g, l16 = it.l16, qw = it.w;
+  const int nsteps = it.nsteps, p_first = it.p_first, p_end = it.p_end, t1 = it.t1;
+
+  // Q^T fragments of row tiles 2 qw + k: lane (row l16, group g) holds bytes
+  // [32 g, 32 g + 32) of each 128-byte K step of its row; the rope step uses groups 0-1.
+  v8i qf[2][5];
+  int lim_q[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int qrow = it.row0 + (2 * qw + k) * kTileRows + l16;
+    const bool valid = qrow < P.rows;
+    const uint8_t* qp = it.q + ((int64_t)it.b * P.rows + (valid ? qrow : 0)) * kDQK;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      v4i a = ld16(qp, 128 * c4 + 32 * g);
+      v4i c = ld16(qp, 128 * c4 + 32 * g + 16);
+      if (!valid) { a = 0; c = 0; }
+      qf[k][c4] = cat8(a, c);
+    }
+    v4i a = ld16(qp, 512 + 32 * (g & 1));
+    v4i c = ld16(qp, 512 + 32 * (g & 1) + 16);
+    if (!valid || g >= 2) { a = 0; c = 0; }
+    qf[k][4] = cat8(a, c);
+    // causal limit of the row: query j sees tokens < L - q_len + j + 1
+    const int jq = valid ? qrow / P.heads : P.q_len - 1;
+    lim_q[k] = min(t1, it.L - P.q_len + jq + 1);
+  }
+  // below this token no row of the wave needs a mask
+  const int first_row = min(it.row0 + 2 * qw * kTileRows, P.rows - 1);
+  const int lim_all = min(t1, it.L - P.q_len + first_row / P.heads + 1);
+
+  // K operand offsets inside a token row (swizzled chunks; rot depends on l16 only).
+  const int rot = l16 >> 2;
+  const int k_off = 16 * (2 * g + rot);  // + 128 c4 (+ 16): no wrap for c4 < 4
+  const int r_off0 = 16 * ((32 + 2 * (g & 1) + rot) % kChunks);
+  const int r_off1 = 16 * ((33 + 2 * (g & 1) + rot) % kChunks);
+
+  // Direct-to-LDS loads: this wave issues loads k = qw kDMA + i (< 36) of every step;
+  // load k fills LDS bytes [1024 k, 1024 k + 1024) of the stage, i.e. 16-byte slots of
+  // page k / 18. Source offsets inside the page, 16 bits each, two per register.
+  uint32_t src2[R::kDMA / 2];
+#pragma unroll
+  for (int i = 0; i < R::kDMA; i += 2) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = qw * R::kDMA + i + h;
+      const int slot = (k % kPageLoads) * 64 + lane;  // 16-byte slot of the page in LDS
+      const int n = slot / kChunks, pos = slot % kChunks;
+      int c = pos - rot_of(n);
+      if (c < 0) c += kChunks;
+      v |= (uint32_t)(n * kDQK + 16 * c) << (16 * h);
+    }
+    src2[i / 2] = v;
+  }
+  auto issue = [&](int st) {
+    const int pa = p_first + st * kStepPages;
+    const int pb = min(pa + 1, p_end - 1);  // odd tail: reload page a (never used)
+    const uint64_t ga = uniform_addr(it.kv + (int64_t)it.btb[pa] * kPageBytes);
+    const uint64_t gb = uniform_addr(it.kv + (int64_t)it.btb[pb] * kPageBytes);
+    uint8_t* stage = sm.pages[st % kStages];
+#pragma unroll
+    for (int i = 0; i < R::kDMA; ++i) {
+      const int k = qw * R::kDMA + i;
+      const uint32_t off = (src2[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      dma16(k >= kPageLoads ? gb : ga, off, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + k * 1024));
+    }
+  };
+
+  // row bookkeeping of rows (2 qw + k) 16 + l16, identical in the four lane groups
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  float lt_run[2] = {0.f, 0.f};
+
+  auto qk_step = [&](int st) {
+    const uint8_t* stage = sm.pages[st % kStages];
+    float cpg[2][kStepPages], xs[2][kStepPages], xt[2][kStepPages];
+#pragma unroll
+    for (int p = 0; p < kStepPages; ++p) {
+      v4f sacc[2][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint8_t* rowp = stage + p * kPageBytes + (16 * tt + l16) * kDQK;
+        v4f a4[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const v8i kf = cat8(ld16(rowp, k_off + 128 * c4), ld16(rowp, k_off + 128 * c4 + 16));
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            a4[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[k][c4], a4[k], 0, 0, 0, 127, 0, 127);
+        }
+        v4i ra = ld16(rowp, r_off0);
+        v4i rb = ld16(rowp, r_off1);
+        if (g >= 2) { ra = 0; rb = 0; }
+        const v8i rf = cat8(ra, rb);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          sacc[k][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, qf[k][4], a4[k], 0, 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane holds S[row l16][page token 16 tt + 4 g + jj]
+      const int tok_page = (p_first + st * kStepPages + p) * kPage;
+      const bool need_mask = tok_page + kPage > lim_all;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float t[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float v = sacc[k][tt][jj] * it.scale_log2;
+            if (need_mask && tok_page + 16 * tt + 4 * g + jj >= lim_q[k]) v = -INFINITY;
+            t[tt][jj] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float c = ceilf(mx);  // -inf when no key of the page is visible to the row
+        const float off = 8.f - (c == -INFINITY ? 0.f : c);
+        float sx = 0.f, sq = 0.f;
+        const int row = (2 * qw + k) * kTileRows + l16;
+        // page token 16 tt + 4 g + jj goes to K position 32 p + 16 (g >> 1) + 8 tt + 4 (g & 1) + jj
+        uint8_t* prow = sm.ptile[st & 1] + row * kPRow + 32 * p + 16 * (g >> 1) + 4 * (g & 1);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float x[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            x[jj] = exp2f(t[tt][jj] + off);  // exp2(-inf) = 0
+            sx += x[jj];
+          }
+          int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hw, true);
+          const float h0 = __builtin_amdgcn_cvt_f32_fp8(hw, 0);
+          const float h1 = __builtin_amdgcn_cvt_f32_fp8(hw, 1);
+          const float h2 = __builtin_amdgcn_cvt_f32_fp8(hw, 2);
+          const float h3 = __builtin_amdgcn_cvt_f32_fp8(hw, 3);
+          int lw = __builtin_amdgcn_cvt_pk_fp8_f32((x[0] - h0) * 16.f, (x[1] - h1) * 16.f, 0, false);
+          lw = __builtin_amdgcn_cvt_pk_fp8_f32((x[2] - h2) * 16.f, (x[3] - h3) * 16.f, lw, true);
+          // P~ = hi + lo / 16 exactly as the PV product weighs it
+          sq += (h0 + h1) + (h2 + h3);
+          sq += ((__builtin_amdgcn_cvt_f32_fp8(lw, 0) + __builtin_amdgcn_cvt_f32_fp8(lw, 1)) +
+                 (__builtin_amdgcn_cvt_f32_fp8(lw, 2) + __builtin_amdgcn_cvt_f32_fp8(lw, 3))) * 0.0625f;
+          *(int*)(prow + 8 * tt) = hw;
+          *(int*)(prow + 64 + 8 * tt) = lw;
+        }
+        sx += __shfl_xor(sx, 16);
+        sx += __shfl_xor(sx, 32);
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        cpg[k][p] = c;
+        xs[k][p] = sx;
+        xt[k][p] = sq;
+      }
+    }
+    // step bookkeeping: new running max, rescale factor, page exponents, l and l~
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float mn = fmaxf(m_run[k], fmaxf(cpg[k][0], cpg[k][1]));
+      const float al = mn == m_run[k] ? 1.f : pow2_diff(m_run[k], mn);
+      const float w0 = pow2_diff(cpg[k][0], mn), w1 = pow2_diff(cpg[k][1], mn);
+      l_run[k] = l_run[k] * al + xs[k][0] * w0 + xs[k][1] * w1;
+      lt_run[k] = lt_run[k] * al + xt[k][0] * w0 + xt[k][1] * w1;
+      m_run[k] = mn;
+      const int row = (2 * qw + k) * kTileRows + l16;
+      if (g == 0) {
+        sm.alpha[st & 1][row] = al;
+        sm.sc[st & 1][row] = make_float2(cpg[k][0] == -INFINITY ? -INFINITY : cpg[k][0] - mn,
+                                         cpg[k][1] == -INFINITY ? -INFINITY : cpg[k][1] - mn);
+      }
+    }
+  };
+
+  // ---- pipeline: 1 + nsteps barriers, like the PV waves
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // Q and step 0 landed
+  block_sync_lds();
+  if (nsteps > 0) qk_step(0);
+  for (int st = 0; st < nsteps; ++st) {
+    wait_vmcnt<0>();  // step st + 1 landed
+    block_sync_lds();
+    if (st + 2 < nsteps) issue(st + 2);
+    if (st + 1 < nsteps) qk_step(st + 1);
+  }
+
+  // ---- (m, l, l~) of the wave's rows
+  if (g == 0) {
+    const int64_t part_row0 = (int64_t)it.part * P.rows;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = it.row0 + (2 * qw + k) * kTileRows + l16;
+      if (row < P.rows)
+        *(float4*)(it.ws_stats + (part_row0 + row) * kStatStride) =
+            make_float4(m_run[k], l_run[k], lt_run[k], 0.f);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ PV waves
+// PV wave (group pv >> 2, quarter pv & 3): O of row tiles [rt0, rt0 + NT/2), dims
+// [128 dq, 128 dq + 128), rescaled by the QK waves' per-step factors.
+template <int NT>
+__device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
+  using R = WRoles<NT>;
+  constexpr int kRT = R::kRTg;
+  const PlanDev& P = *it.P;
+  const int g = it.g, l16 = it.l16;
+  const int nsteps = it.nsteps, p_first = it.p_first, t1 = it.t1;
+  const int pv = it.w - R::kQKW;
+  const int rt0 = (pv >> 2) * kRT;  // row tiles [rt0, rt0 + kRT)
+  const int dq = pv & 3;            // dims [128 dq, 128 dq + 128)
+
+  v4f acc[kRT][8];
+#pragma unroll
+  for (int k = 0; k < kRT; ++k)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[k][d] = v4f{0.f, 0.f, 0.f, 0.f};
+  // transposed V reads: lane (16 G + u), read r names token 16 r + 8 (G & 1) + u / 2 of
+  // page G >> 1 and the 8-byte half u % 2 of a 16-dim chunk; it receives dim
+  // 16 chunk + l16 for 8 tokens.
+  int tr_base[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = 16 * r + 8 * (g & 1) + (l16 >> 1);
+    tr_base[r] = (g >> 1) * kPageBytes + t * kDQK + 16 * (8 * dq + rot_of(t)) + 8 * (l16 & 1);
+  }
+
+  auto pv_step = [&](int st) {
+    const uint8_t* stage = sm.pages[st % kStages];
+    const int pb = st & 1;
+    int sa[kRT];
+    v8i pa[kRT];
+#pragma unroll
+    for (int k = 0; k < kRT; ++k) {
+      const int rt = rt0 + k;
+      // result rows rt 16 + 4 g + jj: rescale when the running max moved
+      const float4 al = *(const float4*)&sm.alpha[pb][rt * kTileRows + 4 * g];
+      const bool rescale = al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f;
+      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          acc[k][d][0] *= al.x; acc[k][d][1] *= al.y;
+          acc[k][d][2] *= al.z; acc[k][d][3] *= al.w;
+        }
+      }
+      // operand row rt 16 + l16: E8M0 scale of K block g = (term g >> 1, page g & 1)
+      const float2 e = sm.sc[pb][rt * kTileRows + l16];
+      const float ep = (g & 1) ? e.y : e.x;
+      sa[k] = ep == -INFINITY ? 127 : max(0, 127 + (int)ep - 4 * (g >> 1));
+      const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 16 * g;
+      pa[k] = cat8(ld16(prow, 0), ld16(prow, 64));
+    }
+    // bytes of tokens past the split's end may be poison: zero them (P~ is 0 there).
+    // Byte j of word w of the V operand is step token 32 (g >> 1) + 16 (w >> 1) +
+    // 8 (g & 1) + 4 (w & 1) + j.
+    uint32_t mk[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    if (st == nsteps - 1) {
+      const int valid = t1 - (p_first + st * kStepPages) * kPage;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (32 * (g >> 1) + 16 * (wd >> 1) + 8 * (g & 1) + 4 * (wd & 1) + j < valid) m |= 0xFFu << (8 * j);
+        mk[wd] = m;
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const v2i b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[0] + 16 * d));
+      const v2i b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[1] + 16 * d));
+      const int x0 = b0.x & mk[0], x1 = b0.y & mk[1], x2 = b1.x & mk[2], x3 = b1.y & mk[3];
+      const v8i vb = v8i{x0, x1, x2, x3, x0, x1, x2, x3};
+#pragma unroll
+      for (int k = 0; k < kRT; ++k)
+        acc[k][d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[k], vb, acc[k][d], 0, 0, 0, sa[k], 0, 127);
+    }
+  };
+
+  // ---- pipeline: 1 + nsteps barriers, like the QK waves
+  block_sync_lds();
+  for (int st = 0; st < nsteps; ++st) {
+    block_sync_lds();
+    pv_step(st);
+  }
+
+  // ---- O partial rows rt 16 + 4 g + jj, dims 128 dq + 16 d + l16
+  const int64_t part_row0 = (int64_t)it.part * P.rows;
+#pragma unroll
+  for (int k = 0; k < kRT; ++k) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = it.row0 + (rt0 + k) * kTileRows + 4 * g + jj;
+      if (row < P.rows) {
+        float* orow = it.ws_o + (part_row0 + row) * kDV + 128 * dq + l16;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) orow[16 * d] = acc[k][d][jj];
+      }
+    }
+  }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(WRoles<NT>::kThreads, 1)
+partial_wide_kernel(const PlanDev P, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                    const int32_t* __restrict__ bt, int64_t bt_stride,
+                    const int32_t* __restrict__ kv_lens, float scale_log2,
+                    float* __restrict__ ws_o, float* __restrict__ ws_stats) {
+  __shared__ WSmem<NT> sm;
+  WItem it;
+  it.lane = threadIdx.x & 63;
+  it.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
+  it.g = it.lane >> 4;
+  it.l16 = it.lane & 15;
+  int ps, blk;
+  if (!wg_item(P, blockIdx.x, &ps, &blk)) return;
+  int e = 0;
+  {
+    int lo = 0, hi = P.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(P.sorted[mid] >> 8) > ps) hi = mid; else lo = mid + 1;
+    }
+    e = lo;
+  }
+  const int b = (int)(P.sorted[e] & 0xFF);
+  const int s = ps - (e > 0 ? (int)(P.sorted[e - 1] >> 8) : 0);
+  it.P = &P;
+  it.q = q;
+  it.kv = kv;
+  it.btb = bt + (int64_t)b * bt_stride;
+  it.ws_o = ws_o;
+  it.ws_stats = ws_stats;
+  it.scale_log2 = scale_log2;
+  it.b = b;
+  it.part = (int)P.part_base[b] + s;
+  it.L = min(kv_lens[b], (int)P.kv_len[b]);
+  const int chunk_tok = chunk_pages_of(P, b) * kPage;
+  const int t0 = s * chunk_tok;
+  it.t1 = max(t0, min(t0 + chunk_tok, it.L));
+  it.row0 = blk * NT * kTileRows;
+  it.p_first = t0 / kPage;
+  it.p_end = (it.t1 + kPage - 1) / kPage;
+  it.nsteps = it.t1 > t0 ? (it.p_end - it.p_first + kStepPages - 1) / kStepPages : 0;
+
+  if (it.w < WRoles<NT>::kQKW) wide_qk<NT>(it, sm);
+  else wide_pv<NT>(it, sm);
+}
+
+}  // namespace
+
+int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                        const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                        float softmax_scale, float* ws_o, float* ws_stats, void* stream) {
+  const PlanDev& P = plan.dev;
+  const int slots = (P.total_parts + 7) / 8;
+  const dim3 grid(8 * slots * P.tiles);
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t st = (hipStream_t)stream;
+  if (P.nt == 4)
+    hipLaunchKernelGGL(partial_wide_kernel<4>, grid, dim3(WRoles<4>::kThreads), 0, st, P, q, kv, bt,
+                       bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+  else
+    hipLaunchKernelGGL(partial_wide_kernel<6>, grid, dim3(WRoles<6>::kThreads), 0, st, P, q, kv, bt,
+                       bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla

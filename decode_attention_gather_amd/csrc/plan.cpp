@@ -67,11 +67,19 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   }
 
   const int32_t rows = q_len * num_heads;
-  // Row blocks: at most 2 MFMA row tiles (32 rows) per workgroup, balanced, so that one
-  // staged page feeds as many rows as the workgroup's registers hold.
+  // Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow
+  // kernel). More rows: blocks of 4 or 6 tiles (wide kernel), as few as 96-row blocks
+  // allow, so that one staged page feeds as many rows as the workgroup holds.
   const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
-  const int32_t tiles = (int32_t)ceil_div(tiles16, kMaxTilesPerBlock);
-  const int32_t nt = (int32_t)ceil_div(tiles16, tiles);
+  int32_t tiles, nt;
+  if (tiles16 <= kMaxTilesPerBlock) {
+    tiles = 1;
+    nt = tiles16;
+  } else {
+    const int32_t blocks = (int32_t)ceil_div(tiles16, kWideMaxTiles);
+    nt = ceil_div(tiles16, blocks) <= 4 ? 4 : kWideMaxTiles;
+    tiles = (int32_t)ceil_div(tiles16, nt);
+  }
   std::vector<int64_t> pages(batch), want;
   for (int32_t b = 0; b < batch; ++b) pages[b] = ceil_div(kv_lens_host[b], kPage);
   want_splits(pages, split_kv, max_split_kv, tiles, num_cus, want);

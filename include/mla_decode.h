@@ -16,7 +16,7 @@
  * (emit_softmax_stats, lse_dtype Float32 in the same listing); it excludes output_scale.
  *
  * Method. The host planner (mla_decode_plan) cuts each request's keys into S_b splits
- * of whole pages. mla_decode_partial runs one workgroup per (split, block of <= 32
+ * of whole pages. mla_decode_partial runs one workgroup per (split, block of <= 96
  * query rows) and writes, per (row, split), an online-softmax partial (max, sum,
  * unnormalised O) in fp32; mla_decode_merge combines each row's partials, with groups of wavefronts
  * folding interleaved subsets of them and rescaling each group result by
@@ -110,7 +110,7 @@ size_t mla_decode_workspace_size(const mla_decode_plan_t* plan);
 typedef struct {
   int32_t batch, q_len, num_heads;
   int32_t rows_per_request; /* q_len * num_heads */
-  int32_t row_tiles;        /* row blocks (<= 32 rows each): workgroups per split */
+  int32_t row_tiles;        /* row blocks (<= 96 rows each): workgroups per split */
   int32_t total_splits;     /* sum_b S_b */
   int32_t work_items;       /* total_splits * row_tiles */
   int32_t merge_groups;     /* wavefront groups per row in the merge (power of 2) */

@@ -48,9 +48,29 @@ def test_uniform_and_short_plans(lens, q, h, split, exp_splits, exp_chunk):
     info, splits, chunk = p.info()
     assert splits == exp_splits and chunk == exp_chunk
     assert info.rows_per_request == q * h
-    assert info.row_tiles == math.ceil(math.ceil(q * h / 16) / 2)  # blocks of <= 32 rows
+    assert info.row_tiles == expected_row_blocks(q * h)
     assert info.total_splits == sum(splits)
     assert info.work_items == sum(splits) * info.row_tiles
+
+
+def expected_row_blocks(rows):
+    """Row blocks of 16-row tiles: one block of <= 2 tiles up to 32 rows, otherwise as
+    few blocks of <= 6 tiles as cover the rows, each rounded up to 4 or 6 tiles."""
+    tiles16 = math.ceil(rows / 16)
+    if tiles16 <= 2:
+        return 1
+    blocks = math.ceil(tiles16 / 6)
+    nt = 4 if math.ceil(tiles16 / blocks) <= 4 else 6
+    return math.ceil(tiles16 / nt)
+
+
+@pytest.mark.parametrize("rows, blocks", [(12, 1), (24, 1), (32, 1), (33, 1), (48, 1), (64, 1),
+                                          (65, 1), (96, 1), (97, 2), (128, 2), (192, 2),
+                                          (768, 8), (4096, 43)])
+def test_row_blocks(rows, blocks):
+    assert expected_row_blocks(rows) == blocks
+    info, _, _ = plan([4096], 1, rows, 2).info()
+    assert info.row_tiles == blocks
 
 
 def check_cover(lens, splits, chunk):

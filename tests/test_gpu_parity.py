@@ -77,6 +77,11 @@ SMALL = [
     ("q1_many_requests", [37 * i + 5 for i in range(1, 20)], 12, 1, 0),
     ("q4_h1_split5", [640, 641], 1, 4, 5),
     ("odd_pages_split2", [3 * 32 + 7, 5 * 32], 12, 1, 2),
+    # row blocks of the wide kernel: 4 tiles (33-64 rows), 6 tiles with padding rows
+    ("q4_h16_rows64", [500, 1234], 16, 4, 3),
+    ("q4_h12_rows48_planner", [77, 2000], 12, 4, 0),
+    ("q7_h12_rows84", [300, 900], 12, 7, 2),
+    ("q8_h16_two_blocks", [64, 4000], 16, 8, 0),
 ]
 
 
@@ -99,22 +104,23 @@ def test_output_scale_and_extreme_scores(mla):
     assert_parity(o, lse, o_ref, lse_ref, "scales")
 
 
-def test_kv_len_one_and_equal_scores(mla):
+@pytest.mark.parametrize("heads", [12, 48, 96])
+def test_kv_len_one_and_equal_scores(mla, heads):
     # one key per request: O is that key's V (exactly representable in BF16)
-    case = inputs.make_case([1, 1, 1], num_heads=12, q_len=1, seed=6, split_kv=1)
-    _say("[gpu] kv_len 1")
+    case = inputs.make_case([1, 1, 1], num_heads=heads, q_len=1, seed=6, split_kv=1)
+    _say(f"[gpu] kv_len 1 H={heads}")
     o, lse, _ = run_gpu(mla, case)
     o_ref, lse_ref = run_oracle(case)
     assert np.array_equal(o, o_ref.astype(np.float32)), "kv_len 1 must return V exactly"
     assert_parity(o, lse, o_ref, lse_ref, "kv_len1")
     # q = 0: equal scores, O = mean of V
-    case = inputs.make_case([100, 1000], num_heads=12, q_len=1, seed=7, split_kv=4)
+    case = inputs.make_case([100, 1000], num_heads=heads, q_len=1, seed=7, split_kv=4)
     case.q.zero_()
-    _say("[gpu] equal scores")
+    _say(f"[gpu] equal scores H={heads}")
     o, lse, _ = run_gpu(mla, case)
     o_ref, lse_ref = run_oracle(case)
     assert_parity(o, lse, o_ref, lse_ref, "equal")
-    np.testing.assert_allclose(lse, np.log([100.0] * 12 + [1000.0] * 12), rtol=1e-6)
+    np.testing.assert_allclose(lse, np.log([100.0] * heads + [1000.0] * heads), rtol=1e-6)
 
 
 def test_split_invariance_f32(mla):
