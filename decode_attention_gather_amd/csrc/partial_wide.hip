@@ -13,24 +13,25 @@
 // feeds 64 or 96 rows, so each KV byte crosses HBM->L2->LDS once per 96 rows and the
 // MFMA units, not the gather, set the pace (these shapes need ~300 flop per KV byte).
 //
-// Design for gfx950: one workgroup of NT/2 + 8 wavefronts per work item.
+// Design for gfx950: one workgroup of 2 + NT wavefronts (at most 2 per SIMD) per item.
 //  * Gather: direct-to-LDS loads (global_load_lds_dwordx4, 1 KB of one page per
-//    instruction) into a 3-stage ring of 2-page steps, issued by the QK waves two steps
+//    instruction) into a 3-stage ring of 2-page steps, issued by the PV waves two steps
 //    ahead. Rows stay 576 bytes (the load writes LDS contiguously); instead, 16-byte
 //    chunk c of token row n sits at chunk (c + ((n >> 2) & 3)) mod 36, which puts the
 //    16 rows of an operand read, and the 16 consecutive rows of a transposed V read, on
 //    distinct LDS banks. VGPR staging would need ~290 VGPRs per step that the MFMA
 //    waves use for operands and accumulators.
-//  * QK^T: QK wave q owns row tiles 2q and 2q + 1 (Q^T of both in VGPRs) and computes
-//    S^T = K Q^T for both pages of the step with v_mfma_scale_f32_16x16x128_f8f6f4;
-//    every K fragment read from LDS feeds two MFMAs. Softmax as in the narrow kernel:
+//  * QK^T: QK wave q owns row tiles [q NT/2, (q + 1) NT/2) (Q^T of all in VGPRs) and
+//    computes S^T = K Q^T for both pages of the step: the 512 latent bytes on
+//    v_mfma_scale_f32_16x16x128_f8f6f4, the 64 rope bytes on two
+//    v_mfma_f32_16x16x32_fp8_fp8; every K fragment read from LDS feeds NT/2 MFMAs. Softmax as in the narrow kernel:
 //    per (row, page) c = ceil(max t), x = 2^(t - c + 8), P~ = hi + lo / 16.
-//    The QK waves also keep each row's running maximum m (an integer), l = sum x and
-//    l~ = sum P~ (summed from the decoded E4M3 bytes), and publish per step the rescale
-//    factor 2^(m_old - m_new) and the page exponents c_page - m_new.
-//  * PV: 8 waves; wave (group gq, quarter dq) accumulates O for row tiles
-//    [gq NT/2, (gq + 1) NT/2) and dims [128 dq, 128 dq + 128): every transposed V read
-//    feeds NT/2 MFMAs. The page exponents enter through the E8M0 block scales.
+//    The QK waves also keep each row's running maximum m (an integer) and l = sum x,
+//    and publish per step the rescale factor 2^(m_old - m_new) and the page exponents
+//    c_page - m_new; l~ = sum P~ comes from one PV MFMA against a tile of ones.
+//  * PV: NT waves; wave (pair pp, half dh) accumulates O for row tiles 2 pp, 2 pp + 1
+//    and dims [256 dh, 256 dh + 256): every transposed V read feeds two MFMAs. The page
+//    exponents enter through the E8M0 block scales.
 //  * Token order inside an MFMA K block: position 16 G + j of a step (G = lane group)
 //    holds token 32 (G >> 1) + 16 (j >> 3) + 8 (G & 1) + (j & 7), so the 32 lanes that
 //    one transposed read serves at a time read 16 consecutive token rows.
@@ -59,17 +60,24 @@ constexpr int kStepLoads = kStepBytes / 1024;        // 36 wave-wide 16-byte loa
 constexpr int kPageLoads = kPageBytes / 1024;        // 18 of them per page
 static_assert(kStepLoads * 1024 == kStepBytes && kPageBytes % 1024 == 0, "1 KB loads tile a step");
 constexpr int kPRow = 144;                           // P~ row: 64 hi, 64 lo, 16 pad
+constexpr int kOnesE4M3 = 0x38383838;                // four E4M3 1.0
 
+// Roles (at most 2 waves per SIMD, so every wave may hold 256 VGPRs):
+//  * 2 QK waves; wave q holds Q^T of row tiles [q NT/2, (q + 1) NT/2) in registers.
+//  * NT PV waves; wave (pair pp, half dh) accumulates O of row tiles 2 pp, 2 pp + 1 and
+//    dims [256 dh, 256 dh + 256), keeps l~ of row tile 2 pp + dh, and issues 36 / NT of
+//    the step's direct-to-LDS loads.
 template <int NT>
 struct WRoles {
   static_assert(NT == 4 || NT == 6, "wide row blocks hold 4 or 6 row tiles");
-  static constexpr int kQKW = NT / 2;                 // QK waves, two row tiles each
-  static constexpr int kPVW = 8;                      // PV waves
+  static constexpr int kQKW = 2;                      // QK waves
+  static constexpr int kQKT = NT / 2;                 // row tiles per QK wave
+  static constexpr int kPVW = NT;                     // PV waves
   static constexpr int kWaves = kQKW + kPVW;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRTg = NT / 2;                 // row tiles per PV group
-  static constexpr int kDMA = kStepLoads / kQKW;      // 1 KB loads per QK wave per step
-  static_assert(kDMA * kQKW == kStepLoads && kDMA % 2 == 0, "even share of the step");
+  static constexpr int kDMA = kStepLoads / kPVW;      // 1 KB loads per PV wave per step
+  static_assert(kDMA * kPVW == kStepLoads && kPageLoads % kDMA == 0, "a wave's loads stay in one page");
+  static_assert(kWaves <= 8, "two waves per SIMD");
 };
 
 template <int NT>
@@ -130,6 +138,21 @@ __device__ __forceinline__ v8i cat8(v4i a, v4i b) {
   return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
+// Max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the
+// VALU lane swaps of gfx950 instead of LDS permutes.
+__device__ __forceinline__ float group_max4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // 2^(a - b) for integer-valued a <= b; 0 when a is -inf.
 __device__ __forceinline__ float pow2_diff(float a, float b) {
   return a == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(a - b));
@@ -158,24 +181,27 @@ struct WItem {
 };
 
 // ------------------------------------------------------------------ QK waves
-// QK wave qw: S^T = K Q^T of both pages of a step for row tiles 2 qw and 2 qw + 1, the
-// per-page softmax (P~ to LDS), and the row bookkeeping: running max m (integer), l and
-// l~, with the step's rescale factor 2^(m_old - m_new) and the block-scale exponents
-// c_page - m_new published for the PV waves. Writes the rows' (m, l, l~) at the end.
+// QK wave qw: S^T = K Q^T of both pages of a step for row tiles qw NT/2 + k, the
+// per-page softmax (P~ to LDS), and the row bookkeeping: running max m (integer) and l,
+// with the step's rescale factor 2^(m_old - m_new) and the block-scale exponents
+// c_page - m_new published for the PV waves. Writes the rows' (m, l) at the end.
 template <int NT>
 __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
   using R = WRoles<NT>;
   const PlanDev& P = *it.P;
-  const int lane = it.lane, g = it.g, l16 = it.l16, qw = it.w;
-  const int nsteps = it.nsteps, p_first = it.p_first, p_end = it.p_end, t1 = it.t1;
+  const int g = it.g, l16 = it.l16, qw = it.w;
+  const int nsteps = it.nsteps, p_first = it.p_first, t1 = it.t1;
 
-  // Q^T fragments of row tiles 2 qw + k: lane (row l16, group g) holds bytes
-  // [32 g, 32 g + 32) of each 128-byte K step of its row; the rope step uses groups 0-1.
-  v8i qf[2][5];
-  int lim_q[2];
+  // Q^T fragments of row tiles qw NT/2 + k: lane (row l16, group g) holds bytes
+  // [32 g, 32 g + 32) of each 128-byte K step of its row (latent, 4 scaled FP8 MFMAs of
+  // K = 128) and 8 bytes of each half of the rope (2 FP8 MFMAs of K = 32).
+  constexpr int kT = R::kQKT;
+  v8i qf[kT][4];
+  long qr[kT][2];
+  int lim_q[kT];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int qrow = it.row0 + (2 * qw + k) * kTileRows + l16;
+  for (int k = 0; k < kT; ++k) {
+    const int qrow = it.row0 + (qw * kT + k) * kTileRows + l16;
     const bool valid = qrow < P.rows;
     const uint8_t* qp = it.q + ((int64_t)it.b * P.rows + (valid ? qrow : 0)) * kDQK;
 #pragma unroll
@@ -185,109 +211,81 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
       if (!valid) { a = 0; c = 0; }
       qf[k][c4] = cat8(a, c);
     }
-    v4i a = ld16(qp, 512 + 32 * (g & 1));
-    v4i c = ld16(qp, 512 + 32 * (g & 1) + 16);
-    if (!valid || g >= 2) { a = 0; c = 0; }
-    qf[k][4] = cat8(a, c);
+    // rope: two K = 32 steps, lane group g holds bytes [8 g, 8 g + 8) of each half
+    qr[k][0] = valid ? *(const long*)(qp + 512 + 8 * g) : 0;
+    qr[k][1] = valid ? *(const long*)(qp + 544 + 8 * g) : 0;
     // causal limit of the row: query j sees tokens < L - q_len + j + 1
     const int jq = valid ? qrow / P.heads : P.q_len - 1;
     lim_q[k] = min(t1, it.L - P.q_len + jq + 1);
   }
   // below this token no row of the wave needs a mask
-  const int first_row = min(it.row0 + 2 * qw * kTileRows, P.rows - 1);
+  const int first_row = min(it.row0 + qw * kT * kTileRows, P.rows - 1);
   const int lim_all = min(t1, it.L - P.q_len + first_row / P.heads + 1);
 
   // K operand offsets inside a token row (swizzled chunks; rot depends on l16 only).
   const int rot = l16 >> 2;
   const int k_off = 16 * (2 * g + rot);  // + 128 c4 (+ 16): no wrap for c4 < 4
-  const int r_off0 = 16 * ((32 + 2 * (g & 1) + rot) % kChunks);
-  const int r_off1 = 16 * ((33 + 2 * (g & 1) + rot) % kChunks);
+  const int r_off0 = 16 * ((32 + (g >> 1) + rot) % kChunks) + 8 * (g & 1);
+  const int r_off1 = 16 * ((34 + (g >> 1) + rot) % kChunks) + 8 * (g & 1);
 
-  // Direct-to-LDS loads: this wave issues loads k = qw kDMA + i (< 36) of every step;
-  // load k fills LDS bytes [1024 k, 1024 k + 1024) of the stage, i.e. 16-byte slots of
-  // page k / 18. Source offsets inside the page, 16 bits each, two per register.
-  uint32_t src2[R::kDMA / 2];
+  // row bookkeeping of rows (qw NT/2 + k) 16 + l16: m identical in the four lane groups,
+  // l kept per lane over the lane's own tokens and summed over the groups at the end
+  float m_run[kT], l_run[kT];
 #pragma unroll
-  for (int i = 0; i < R::kDMA; i += 2) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = qw * R::kDMA + i + h;
-      const int slot = (k % kPageLoads) * 64 + lane;  // 16-byte slot of the page in LDS
-      const int n = slot / kChunks, pos = slot % kChunks;
-      int c = pos - rot_of(n);
-      if (c < 0) c += kChunks;
-      v |= (uint32_t)(n * kDQK + 16 * c) << (16 * h);
-    }
-    src2[i / 2] = v;
-  }
-  auto issue = [&](int st) {
-    const int pa = p_first + st * kStepPages;
-    const int pb = min(pa + 1, p_end - 1);  // odd tail: reload page a (never used)
-    const uint64_t ga = uniform_addr(it.kv + (int64_t)it.btb[pa] * kPageBytes);
-    const uint64_t gb = uniform_addr(it.kv + (int64_t)it.btb[pb] * kPageBytes);
-    uint8_t* stage = sm.pages[st % kStages];
-#pragma unroll
-    for (int i = 0; i < R::kDMA; ++i) {
-      const int k = qw * R::kDMA + i;
-      const uint32_t off = (src2[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-      dma16(k >= kPageLoads ? gb : ga, off, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + k * 1024));
-    }
-  };
-
-  // row bookkeeping of rows (2 qw + k) 16 + l16, identical in the four lane groups
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  float lt_run[2] = {0.f, 0.f};
+  for (int k = 0; k < kT; ++k) { m_run[k] = -INFINITY; l_run[k] = 0.f; }
 
   auto qk_step = [&](int st) {
     const uint8_t* stage = sm.pages[st % kStages];
-    float cpg[2][kStepPages], xs[2][kStepPages], xt[2][kStepPages];
+    float cpg[kT][kStepPages], xs[kT][kStepPages];
 #pragma unroll
     for (int p = 0; p < kStepPages; ++p) {
-      v4f sacc[2][2];
+      v4f sacc[kT][2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const uint8_t* rowp = stage + p * kPageBytes + (16 * tt + l16) * kDQK;
-        v4f a4[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+        v4f a4[kT];
+#pragma unroll
+        for (int k = 0; k < kT; ++k) a4[k] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const v8i kf = cat8(ld16(rowp, k_off + 128 * c4), ld16(rowp, k_off + 128 * c4 + 16));
 #pragma unroll
-          for (int k = 0; k < 2; ++k)
+          for (int k = 0; k < kT; ++k)
             a4[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[k][c4], a4[k], 0, 0, 0, 127, 0, 127);
         }
-        v4i ra = ld16(rowp, r_off0);
-        v4i rb = ld16(rowp, r_off1);
-        if (g >= 2) { ra = 0; rb = 0; }
-        const v8i rf = cat8(ra, rb);
+        const long r0 = *(const long*)(rowp + r_off0);
+        const long r1 = *(const long*)(rowp + r_off1);
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-          sacc[k][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rf, qf[k][4], a4[k], 0, 0, 0, 127, 0, 127);
+        for (int k = 0; k < kT; ++k) {
+          const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r0, qr[k][0], a4[k], 0, 0, 0);
+          sacc[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r1, qr[k][1], a, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane holds S[row l16][page token 16 tt + 4 g + jj]
       const int tok_page = (p_first + st * kStepPages + p) * kPage;
       const bool need_mask = tok_page + kPage > lim_all;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < kT; ++k) {
         float t[2][4];
-        float mx = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float v = sacc[k][tt][jj] * it.scale_log2;
-            if (need_mask && tok_page + 16 * tt + 4 * g + jj >= lim_q[k]) v = -INFINITY;
-            t[tt][jj] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+          for (int jj = 0; jj < 4; ++jj) t[tt][jj] = sacc[k][tt][jj] * it.scale_log2;
+        if (need_mask) {  // uniform: only pages that reach the split's end or a causal limit
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (tok_page + 16 * tt + 4 * g + jj >= lim_q[k]) t[tt][jj] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
+                         fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
+        mx = group_max4(mx);
         const float c = ceilf(mx);  // -inf when no key of the page is visible to the row
         const float off = 8.f - (c == -INFINITY ? 0.f : c);
-        float sx = 0.f, sq = 0.f;
-        const int row = (2 * qw + k) * kTileRows + l16;
+        float sx = 0.f;
+        const int row = (qw * kT + k) * kTileRows + l16;
         // page token 16 tt + 4 g + jj goes to K position 32 p + 16 (g >> 1) + 8 tt + 4 (g & 1) + jj
         uint8_t* prow = sm.ptile[st & 1] + row * kPRow + 32 * p + 16 * (g >> 1) + 4 * (g & 1);
 #pragma unroll
@@ -295,7 +293,7 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
           float x[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            x[jj] = exp2f(t[tt][jj] + off);  // exp2(-inf) = 0
+            x[jj] = __builtin_amdgcn_exp2f(t[tt][jj] + off);  // v_exp_f32; exp2(-inf) = 0
             sx += x[jj];
           }
           int hw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
@@ -306,32 +304,22 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
           const float h3 = __builtin_amdgcn_cvt_f32_fp8(hw, 3);
           int lw = __builtin_amdgcn_cvt_pk_fp8_f32((x[0] - h0) * 16.f, (x[1] - h1) * 16.f, 0, false);
           lw = __builtin_amdgcn_cvt_pk_fp8_f32((x[2] - h2) * 16.f, (x[3] - h3) * 16.f, lw, true);
-          // P~ = hi + lo / 16 exactly as the PV product weighs it
-          sq += (h0 + h1) + (h2 + h3);
-          sq += ((__builtin_amdgcn_cvt_f32_fp8(lw, 0) + __builtin_amdgcn_cvt_f32_fp8(lw, 1)) +
-                 (__builtin_amdgcn_cvt_f32_fp8(lw, 2) + __builtin_amdgcn_cvt_f32_fp8(lw, 3))) * 0.0625f;
           *(int*)(prow + 8 * tt) = hw;
           *(int*)(prow + 64 + 8 * tt) = lw;
         }
-        sx += __shfl_xor(sx, 16);
-        sx += __shfl_xor(sx, 32);
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
         cpg[k][p] = c;
         xs[k][p] = sx;
-        xt[k][p] = sq;
       }
     }
-    // step bookkeeping: new running max, rescale factor, page exponents, l and l~
+    // step bookkeeping: new running max, rescale factor, page exponents, l
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kT; ++k) {
       const float mn = fmaxf(m_run[k], fmaxf(cpg[k][0], cpg[k][1]));
       const float al = mn == m_run[k] ? 1.f : pow2_diff(m_run[k], mn);
       const float w0 = pow2_diff(cpg[k][0], mn), w1 = pow2_diff(cpg[k][1], mn);
       l_run[k] = l_run[k] * al + xs[k][0] * w0 + xs[k][1] * w1;
-      lt_run[k] = lt_run[k] * al + xt[k][0] * w0 + xt[k][1] * w1;
       m_run[k] = mn;
-      const int row = (2 * qw + k) * kTileRows + l16;
+      const int row = (qw * kT + k) * kTileRows + l16;
       if (g == 0) {
         sm.alpha[st & 1][row] = al;
         sm.sc[st & 1][row] = make_float2(cpg[k][0] == -INFINITY ? -INFINITY : cpg[k][0] - mn,
@@ -341,50 +329,83 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
   };
 
   // ---- pipeline: 1 + nsteps barriers, like the PV waves
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
-  if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // Q and step 0 landed
-  block_sync_lds();
+  __builtin_amdgcn_s_setprio(2);  // the QK waves pace the step: issue first on their SIMD
+  block_sync_lds();  // step 0 landed
   if (nsteps > 0) qk_step(0);
   for (int st = 0; st < nsteps; ++st) {
-    wait_vmcnt<0>();  // step st + 1 landed
     block_sync_lds();
-    if (st + 2 < nsteps) issue(st + 2);
     if (st + 1 < nsteps) qk_step(st + 1);
   }
 
-  // ---- (m, l, l~) of the wave's rows
+  // ---- (m, l) of the wave's rows (l~ comes from the PV waves)
+#pragma unroll
+  for (int k = 0; k < kT; ++k) l_run[k] = group_sum4(l_run[k]);
   if (g == 0) {
     const int64_t part_row0 = (int64_t)it.part * P.rows;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int row = it.row0 + (2 * qw + k) * kTileRows + l16;
+    for (int k = 0; k < kT; ++k) {
+      const int row = it.row0 + (qw * kT + k) * kTileRows + l16;
       if (row < P.rows)
-        *(float4*)(it.ws_stats + (part_row0 + row) * kStatStride) =
-            make_float4(m_run[k], l_run[k], lt_run[k], 0.f);
+        *(float2*)(it.ws_stats + (part_row0 + row) * kStatStride) = make_float2(m_run[k], l_run[k]);
     }
   }
 }
 
 // ------------------------------------------------------------------ PV waves
-// PV wave (group pv >> 2, quarter pv & 3): O of row tiles [rt0, rt0 + NT/2), dims
-// [128 dq, 128 dq + 128), rescaled by the QK waves' per-step factors.
+// PV wave (pair pv >> 1, half pv & 1): O of row tiles rt0, rt0 + 1 and dims
+// [256 dh, 256 dh + 256), rescaled by the QK waves' per-step factors; l~ of row tile
+// rt0 + dh; and loads pv kDMA .. pv kDMA + kDMA - 1 of every step.
 template <int NT>
 __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   using R = WRoles<NT>;
-  constexpr int kRT = R::kRTg;
+  constexpr int kRT = 2;   // row tiles per PV wave
+  constexpr int kDT = 16;  // 16-dim tiles per PV wave
   const PlanDev& P = *it.P;
   const int g = it.g, l16 = it.l16;
   const int nsteps = it.nsteps, p_first = it.p_first, t1 = it.t1;
   const int pv = it.w - R::kQKW;
-  const int rt0 = (pv >> 2) * kRT;  // row tiles [rt0, rt0 + kRT)
-  const int dq = pv & 3;            // dims [128 dq, 128 dq + 128)
+  const int rt0 = (pv >> 1) * kRT;  // row tiles [rt0, rt0 + 2)
+  const int dh = pv & 1;             // dims [256 dh, 256 dh + 256)
+  const int lane = it.lane, p_end = it.p_end;
 
-  v4f acc[kRT][8];
+  // Direct-to-LDS loads: loads k = pv kDMA + i of every step, all in page (pv kDMA) / 18;
+  // load k fills LDS bytes [1024 k, 1024 k + 1024) of the stage. Source offsets inside
+  // the page, 16 bits each, two per register.
+  uint32_t src2[(R::kDMA + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < R::kDMA; i += 2) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int h = 0; h < 2 && i + h < R::kDMA; ++h) {
+      const int k = pv * R::kDMA + i + h;
+      const int slot = (k % kPageLoads) * 64 + lane;  // 16-byte slot of the page in LDS
+      const int n = slot / kChunks, pos = slot % kChunks;
+      int c = pos - rot_of(n);
+      if (c < 0) c += kChunks;
+      v |= (uint32_t)(n * kDQK + 16 * c) << (16 * h);
+    }
+    src2[i / 2] = v;
+  }
+  const bool ld_page_b = (pv * R::kDMA) >= kPageLoads;
+  auto issue = [&](int st) {
+    const int pa = p_first + st * kStepPages;
+    const int pg = ld_page_b ? min(pa + 1, p_end - 1) : pa;  // odd tail: reload page a
+    const uint64_t gp = uniform_addr(it.kv + (int64_t)it.btb[pg] * kPageBytes);
+    uint8_t* stage = sm.pages[st % kStages];
+#pragma unroll
+    for (int i = 0; i < R::kDMA; ++i) {
+      const int k = pv * R::kDMA + i;
+      const uint32_t off = (src2[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      dma16(gp, off, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + k * 1024));
+    }
+  };
+
+  v4f acc[kRT][kDT];
+  v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile rt0 + dh: ones product
 #pragma unroll
   for (int k = 0; k < kRT; ++k)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) acc[k][d] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < kDT; ++d) acc[k][d] = v4f{0.f, 0.f, 0.f, 0.f};
   // transposed V reads: lane (16 G + u), read r names token 16 r + 8 (G & 1) + u / 2 of
   // page G >> 1 and the 8-byte half u % 2 of a 16-dim chunk; it receives dim
   // 16 chunk + l16 for 8 tokens.
@@ -392,7 +413,7 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int t = 16 * r + 8 * (g & 1) + (l16 >> 1);
-    tr_base[r] = (g >> 1) * kPageBytes + t * kDQK + 16 * (8 * dq + rot_of(t)) + 8 * (l16 & 1);
+    tr_base[r] = (g >> 1) * kPageBytes + t * kDQK + 16 * (kDT * dh + rot_of(t)) + 8 * (l16 & 1);
   }
 
   auto pv_step = [&](int st) {
@@ -408,9 +429,12 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
       const bool rescale = al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f;
       if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
+        for (int d = 0; d < kDT; ++d) {
           acc[k][d][0] *= al.x; acc[k][d][1] *= al.y;
           acc[k][d][2] *= al.z; acc[k][d][3] *= al.w;
+        }
+        if (k == dh) {
+          acc1[0] *= al.x; acc1[1] *= al.y; acc1[2] *= al.z; acc1[3] *= al.w;
         }
       }
       // operand row rt 16 + l16: E8M0 scale of K block g = (term g >> 1, page g & 1)
@@ -419,6 +443,11 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
       sa[k] = ep == -INFINITY ? 127 : max(0, 127 + (int)ep - 4 * (g >> 1));
       const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 16 * g;
       pa[k] = cat8(ld16(prow, 0), ld16(prow, 64));
+      if (k == dh) {
+        const v8i ones = v8i{kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
+                             kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[k], ones, acc1, 0, 0, 0, sa[k], 0, 127);
+      }
     }
     // bytes of tokens past the split's end may be poison: zero them (P~ is 0 there).
     // Byte j of word w of the V operand is step token 32 (g >> 1) + 16 (w >> 1) +
@@ -436,7 +465,7 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
       }
     }
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < kDT; ++d) {
       const v2i b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[0] + 16 * d));
       const v2i b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[1] + 16 * d));
       const int x0 = b0.x & mk[0], x1 = b0.y & mk[1], x2 = b1.x & mk[2], x3 = b1.y & mk[3];
@@ -448,13 +477,18 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   };
 
   // ---- pipeline: 1 + nsteps barriers, like the QK waves
+  if (nsteps > 0) issue(0);
+  if (nsteps > 1) issue(1);
+  if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // step 0 landed
   block_sync_lds();
   for (int st = 0; st < nsteps; ++st) {
+    wait_vmcnt<0>();  // step st + 1 landed
     block_sync_lds();
+    if (st + 2 < nsteps) issue(st + 2);
     pv_step(st);
   }
 
-  // ---- O partial rows rt 16 + 4 g + jj, dims 128 dq + 16 d + l16
+  // ---- O partial rows rt 16 + 4 g + jj, dims 256 dh + 16 d + l16
   const int64_t part_row0 = (int64_t)it.part * P.rows;
 #pragma unroll
   for (int k = 0; k < kRT; ++k) {
@@ -462,9 +496,10 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     for (int jj = 0; jj < 4; ++jj) {
       const int row = it.row0 + (rt0 + k) * kTileRows + 4 * g + jj;
       if (row < P.rows) {
-        float* orow = it.ws_o + (part_row0 + row) * kDV + 128 * dq + l16;
+        float* orow = it.ws_o + (part_row0 + row) * kDV + 256 * dh + l16;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) orow[16 * d] = acc[k][d][jj];
+        for (int d = 0; d < kDT; ++d) orow[16 * d] = acc[k][d][jj];
+        if (k == dh && l16 == 0) it.ws_stats[(part_row0 + row) * kStatStride + 2] = acc1[jj];
       }
     }
   }
