@@ -27,7 +27,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int check_workspace(const mla_decode_plan_s* plan, const void* ws, size_t bytes) {
   if (ws == nullptr || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
-  if (bytes < plan->ws_o_bytes + plan->ws_stats_bytes) return MLA_ERR_WORKSPACE;
+  if (bytes < plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes)
+    return MLA_ERR_WORKSPACE;
   return MLA_OK;
 }
 
@@ -42,9 +43,13 @@ int check_partial(const mla_decode_plan_s* plan, const void* q, const void* kv,
     return MLA_ERR_INVALID_ARG;
   // every request's pages must fit its block-table row
   int64_t max_pages = 0;
-  for (int32_t b = 0; b < plan->dev.batch; ++b) {
-    const int64_t p = ((int64_t)plan->kv_lens[b] + kPage - 1) / kPage;
-    if (p > max_pages) max_pages = p;
+  if (plan->device_lengths) {
+    max_pages = ((int64_t)plan->max_kv_len + kPage - 1) / kPage;
+  } else {
+    for (int32_t b = 0; b < plan->dev.batch; ++b) {
+      const int64_t p = ((int64_t)plan->kv_lens[b] + kPage - 1) / kPage;
+      if (p > max_pages) max_pages = p;
+    }
   }
   if (bt_stride < max_pages) return MLA_ERR_INVALID_ARG;
   return check_workspace(plan, ws, ws_bytes);
@@ -61,9 +66,11 @@ int check_merge(const mla_decode_plan_s* plan, const void* ws, size_t ws_bytes,
 
 int hip_status(int e) { return e == (int)hipSuccess ? MLA_OK : MLA_ERR_HIP_BASE - e; }
 
-float* ws_o_of(const mla_decode_plan_s* plan, const void* ws) { return (float*)ws; }
+float* ws_o_of(const mla_decode_plan_s* plan, const void* ws) {
+  return (float*)((uint8_t*)ws + plan->ws_plan_bytes);
+}
 float* ws_stats_of(const mla_decode_plan_s* plan, const void* ws) {
-  return (float*)((uint8_t*)ws + plan->ws_o_bytes);
+  return (float*)((uint8_t*)ws + plan->ws_plan_bytes + plan->ws_o_bytes);
 }
 
 }  // namespace
@@ -77,6 +84,7 @@ int mla_decode_partial(const mla_decode_plan_t* plan, const void* q, const void*
                        const int32_t* block_table, int64_t bt_stride,
                        const int32_t* kv_lens, float softmax_scale, void* workspace,
                        size_t workspace_bytes, void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
   int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
                          workspace, workspace_bytes);
   if (rc != MLA_OK) return rc;
@@ -89,6 +97,7 @@ int mla_decode_partial(const mla_decode_plan_t* plan, const void* q, const void*
 int mla_decode_merge(const mla_decode_plan_t* plan, const void* workspace,
                      size_t workspace_bytes, float output_scale, void* o, float* lse,
                      void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
   int rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
   if (rc != MLA_OK) return rc;
   return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
@@ -98,6 +107,7 @@ int mla_decode_merge(const mla_decode_plan_t* plan, const void* workspace,
 int mla_decode_merge_f32(const mla_decode_plan_t* plan, const void* workspace,
                          size_t workspace_bytes, float output_scale, float* o, float* lse,
                          void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
   int rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
   if (rc != MLA_OK) return rc;
   return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
@@ -108,6 +118,7 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
                const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
                float softmax_scale, float output_scale, void* workspace,
                size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
   int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
                          workspace, workspace_bytes);
   if (rc != MLA_OK) return rc;
@@ -119,6 +130,32 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
   if (rc != MLA_OK) return rc;
   return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
                                  output_scale, o, false, lse, stream));
+}
+
+int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                     const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                     const float* softmax_scale, const float* output_scale, void* workspace,
+                     size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (plan == nullptr || !plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if (softmax_scale == nullptr || output_scale == nullptr || !aligned(softmax_scale, 4) ||
+      !aligned(output_scale, 4))
+    return MLA_ERR_INVALID_ARG;
+  // the scale values live on the device: a finite placeholder passes the host check
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, 1.f, workspace,
+                         workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  rc = check_merge(plan, workspace, workspace_bytes, 1.f, o, lse);
+  if (rc != MLA_OK) return rc;
+  PlanDev* pdev = (PlanDev*)workspace;
+  const DeviceArgs dev{pdev, softmax_scale, output_scale};
+  rc = hip_status(launch_device_plan(*plan, kv_lens, pdev, stream));
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache, block_table,
+                                 bt_stride, kv_lens, 1.f, ws_o_of(plan, workspace),
+                                 ws_stats_of(plan, workspace), stream, &dev));
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace), 1.f,
+                                 o, false, lse, stream, &dev));
 }
 
 const char* mla_decode_strerror(int status) {

@@ -44,11 +44,18 @@ struct MergeSmem {
   float lt[kMaxGroups];
 };
 
-template <bool kF32Out>
+// kDev: the plan and output_scale come from device memory (graph path).
+template <bool kF32Out, bool kDev>
 __global__ void __launch_bounds__(64 * kMaxGroups)
-merge_kernel(const PlanDev P, const float* __restrict__ ws_o, const float* __restrict__ ws_stats,
-             float output_scale, void* __restrict__ out, float* __restrict__ lse, int groups) {
+merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
+             const float* __restrict__ oscale_dev, const float* __restrict__ ws_o,
+             const float* __restrict__ ws_stats, float output_scale_arg, void* __restrict__ out,
+             float* __restrict__ lse, int groups) {
   __shared__ MergeSmem sm;
+  const PlanDev& P = kDev ? *pdev : Parg;
+  const float output_scale = kDev ? *oscale_dev : output_scale_arg;
+  // groups in use: the launch's, or the device plan's (<= the launch's) on the graph path
+  const int G = kDev ? min(P.groups, groups) : groups;
   const int row_global = blockIdx.x;  // (b * q_len + j) * H + h
   const int b = row_global / P.rows;
   const int r = row_global - b * P.rows;
@@ -59,11 +66,11 @@ merge_kernel(const PlanDev P, const float* __restrict__ ws_o, const float* __res
 
   float M = -INFINITY, l = 0.f, lt = 0.f;
   float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-  for (int s0 = gw; s0 < S; s0 += kUnroll * groups) {
+  for (int s0 = gw; gw < G && s0 < S; s0 += kUnroll * G) {
     float4 stv[kUnroll], a[kUnroll], c[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int s = s0 + u * groups;
+      const int s = s0 + u * G;
       if (s < S) {
         const int64_t pr = (int64_t)(base + s) * P.rows + r;
         stv[u] = *(const float4*)(ws_stats + pr * kStatStride);
@@ -101,18 +108,18 @@ merge_kernel(const PlanDev P, const float* __restrict__ ws_o, const float* __res
   __syncthreads();
 
   float Mx = -INFINITY;
-  for (int k = 0; k < groups; ++k) Mx = fmaxf(Mx, sm.m[k]);
+  for (int k = 0; k < G; ++k) Mx = fmaxf(Mx, sm.m[k]);
   float wk[kMaxGroups];
   float L = 0.f, Lt = 0.f;
-  for (int k = 0; k < groups; ++k) {
+  for (int k = 0; k < G; ++k) {
     wk[k] = Mx == -INFINITY ? 0.f : pow2i(sm.m[k], Mx);
     L += wk[k] * sm.l[k];
     Lt += wk[k] * sm.lt[k];
   }
   const float inv = Lt > 0.f ? output_scale / Lt : 0.f;
-  for (int d = threadIdx.x; d < kDV; d += 64 * groups) {
+  for (int d = threadIdx.x; d < kDV; d += blockDim.x) {
     float acc = 0.f;
-    for (int k = 0; k < groups; ++k) acc += wk[k] * sm.o[k][d];
+    for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d];
     const float v = acc * inv;
     if (kF32Out)
       ((float*)out)[(int64_t)row_global * kDV + d] = v;
@@ -126,16 +133,26 @@ merge_kernel(const PlanDev P, const float* __restrict__ ws_o, const float* __res
 }  // namespace
 
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
-                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream) {
+                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
+                 const DeviceArgs* dev) {
   const PlanDev& P = plan.dev;
   const int rows_total = P.batch * P.rows;
   const int groups = plan.merge_groups;
-  if (o_is_f32)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(rows_total), dim3(64 * groups), 0,
-                       (hipStream_t)stream, P, ws_o, ws_stats, output_scale, o, lse, groups);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(rows_total), dim3(64 * groups), 0,
-                       (hipStream_t)stream, P, ws_o, ws_stats, output_scale, o, lse, groups);
+  const PlanDev* pd = dev ? dev->plan : nullptr;
+  const float* od = dev ? dev->output_scale : nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid(rows_total), block(64 * groups);
+  if (o_is_f32) {
+    if (dev)
+      hipLaunchKernelGGL((merge_kernel<true, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+    else
+      hipLaunchKernelGGL((merge_kernel<true, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+  } else {
+    if (dev)
+      hipLaunchKernelGGL((merge_kernel<false, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+    else
+      hipLaunchKernelGGL((merge_kernel<false, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+  }
   return (int)hipGetLastError();
 }
 

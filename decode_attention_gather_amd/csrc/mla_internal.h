@@ -39,7 +39,7 @@ struct PlanDev {
   int32_t tiles;        // row blocks (workgroups) per split: ceil(rows / (16 nt))
   int32_t total_parts;  // sum of splits
   int32_t nt;           // 16-row tiles per row block: 1, 2 (narrow) or 4, 6 (wide)
-  int32_t pad1;
+  int32_t groups;       // merge: wavefront groups per row (<= the launch's groups)
   uint32_t sorted[kMaxBatch];     // (part_end << 8) | request
   uint32_t kv_len[kMaxBatch];     // per request: the plan's (host) length
   uint32_t part_base[kMaxBatch];  // per request: index of its first split
@@ -54,9 +54,17 @@ __host__ __device__ inline int chunk_pages_of(const PlanDev& P, int b) {
 
 }  // namespace mla
 
-// Host-side plan object (opaque to callers).
+// Host-side plan object (opaque to callers). A graph plan (device_lengths != 0) holds
+// capacities only: the request lengths stay on the device, a planner kernel writes the
+// PlanDev into the head of the workspace on every call, and dev.total_parts is the
+// capacity the launches are sized for.
 struct mla_decode_plan_s {
   mla::PlanDev dev;
+  int32_t device_lengths;
+  int32_t max_kv_len;     // graph plans: upper bound of every device length
+  int32_t split_kv;       // graph plans: the uniform bound, 0 = proportional planner
+  int32_t max_split_kv;   // graph plans: per-request split cap
+  size_t ws_plan_bytes;   // graph plans: device PlanDev at the head of the workspace
   int32_t merge_groups;
   int32_t max_splits;
   int32_t num_cus;
@@ -70,14 +78,28 @@ namespace mla {
 // Workspace carve-up: partial O at offset 0, stats after it (256-byte aligned).
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Launchers (defined next to their kernels). Return a hipError_t value as int.
+// Graph path: where the kernels find the plan and the scales (device memory).
+struct DeviceArgs {
+  const PlanDev* plan;
+  const float* softmax_scale;
+  const float* output_scale;
+};
+
+// Launchers (defined next to their kernels). Return a hipError_t value as int. With
+// dev != nullptr the kernels read the plan and the scales from device memory and the
+// launch is sized by the plan's capacity.
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
-                   float softmax_scale, float* ws_o, float* ws_stats, void* stream);
+                   float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                   const DeviceArgs* dev = nullptr);
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
-                        float softmax_scale, float* ws_o, float* ws_stats, void* stream);
+                        float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                        const DeviceArgs* dev);
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
-                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream);
+                 float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
+                 const DeviceArgs* dev = nullptr);
+int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,
+                       void* stream);
 
 }  // namespace mla

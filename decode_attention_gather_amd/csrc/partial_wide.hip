@@ -505,13 +505,17 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   }
 }
 
-template <int NT>
+// kDev: the plan and the softmax scale come from device memory (graph path).
+template <int NT, bool kDev>
 __global__ void __launch_bounds__(WRoles<NT>::kThreads, 1)
-partial_wide_kernel(const PlanDev P, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kv,
-                    const int32_t* __restrict__ bt, int64_t bt_stride,
-                    const int32_t* __restrict__ kv_lens, float scale_log2,
+partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
+                    const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
+                    const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt,
+                    int64_t bt_stride, const int32_t* __restrict__ kv_lens, float scale_log2_arg,
                     float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ WSmem<NT> sm;
+  const PlanDev& P = kDev ? *pdev : Parg;
+  const float scale_log2 = kDev ? *scale_dev * 1.4426950408889634f : scale_log2_arg;
   WItem it;
   it.lane = threadIdx.x & 63;
   it.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
@@ -556,18 +560,30 @@ partial_wide_kernel(const PlanDev P, const uint8_t* __restrict__ q, const uint8_
 
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
-                        float softmax_scale, float* ws_o, float* ws_stats, void* stream) {
+                        float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                        const DeviceArgs* dev) {
   const PlanDev& P = plan.dev;
-  const int slots = (P.total_parts + 7) / 8;
+  const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  const PlanDev* pd = dev ? dev->plan : nullptr;
+  const float* sd = dev ? dev->softmax_scale : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  if (P.nt == 4)
-    hipLaunchKernelGGL(partial_wide_kernel<4>, grid, dim3(WRoles<4>::kThreads), 0, st, P, q, kv, bt,
-                       bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
-  else
-    hipLaunchKernelGGL(partial_wide_kernel<6>, grid, dim3(WRoles<6>::kThreads), 0, st, P, q, kv, bt,
-                       bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+  if (P.nt == 4) {
+    if (dev)
+      hipLaunchKernelGGL((partial_wide_kernel<4, true>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
+                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+    else
+      hipLaunchKernelGGL((partial_wide_kernel<4, false>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
+                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+  } else {
+    if (dev)
+      hipLaunchKernelGGL((partial_wide_kernel<6, true>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
+                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+    else
+      hipLaunchKernelGGL((partial_wide_kernel<6, false>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
+                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+  }
   return (int)hipGetLastError();
 }
 

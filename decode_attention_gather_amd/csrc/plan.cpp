@@ -46,6 +46,30 @@ void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t ma
   }
 }
 
+// Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow
+// kernel). More rows: blocks of 4 or 6 tiles (wide kernel), as few as 96-row blocks
+// allow, so that one staged page feeds as many rows as the workgroup holds.
+void row_blocks(int32_t rows, int32_t* tiles, int32_t* nt) {
+  const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
+  if (tiles16 <= kMaxTilesPerBlock) {
+    *tiles = 1;
+    *nt = tiles16;
+  } else {
+    const int32_t blocks = (int32_t)ceil_div(tiles16, kWideMaxTiles);
+    *nt = ceil_div(tiles16, blocks) <= 4 ? 4 : kWideMaxTiles;
+    *tiles = (int32_t)ceil_div(tiles16, *nt);
+  }
+}
+
+// Merge width: wavefront groups per row, a power of two <= min(16, max splits), halved
+// while rows * groups exceeds 8 waves per CU.
+int32_t merge_groups_for(int64_t max_s, int64_t rows_total, int32_t num_cus) {
+  int32_t g = 1;
+  while (g * 2 <= 16 && g * 2 <= max_s) g *= 2;
+  while (g > 1 && rows_total * g > 8LL * num_cus) g /= 2;
+  return g;
+}
+
 }  // namespace
 
 int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
@@ -67,19 +91,8 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   }
 
   const int32_t rows = q_len * num_heads;
-  // Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow
-  // kernel). More rows: blocks of 4 or 6 tiles (wide kernel), as few as 96-row blocks
-  // allow, so that one staged page feeds as many rows as the workgroup holds.
-  const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
   int32_t tiles, nt;
-  if (tiles16 <= kMaxTilesPerBlock) {
-    tiles = 1;
-    nt = tiles16;
-  } else {
-    const int32_t blocks = (int32_t)ceil_div(tiles16, kWideMaxTiles);
-    nt = ceil_div(tiles16, blocks) <= 4 ? 4 : kWideMaxTiles;
-    tiles = (int32_t)ceil_div(tiles16, nt);
-  }
+  row_blocks(rows, &tiles, &nt);
   std::vector<int64_t> pages(batch), want;
   for (int32_t b = 0; b < batch; ++b) pages[b] = ceil_div(kv_lens_host[b], kPage);
   want_splits(pages, split_kv, max_split_kv, tiles, num_cus, want);
@@ -134,13 +147,8 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     d.sorted[e] = (run << 8) | (uint32_t)order[e];
   }
 
-  // Merge width: wavefront groups per row, a power of two <= min(16, max splits),
-  // halved while rows * groups exceeds 8 waves per CU.
-  int32_t g = 1;
-  while (g * 2 <= 16 && g * 2 <= max_s) g *= 2;
-  const int64_t rows_total = (int64_t)batch * rows;
-  while (g > 1 && rows_total * g > 8LL * num_cus) g /= 2;
-  plan->merge_groups = g;
+  plan->merge_groups = merge_groups_for(max_s, (int64_t)batch * rows, num_cus);
+  d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)max_s;
   plan->num_cus = num_cus;
   plan->ws_o_bytes = align256((size_t)total * rows * kDV * sizeof(float));
@@ -149,9 +157,82 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   return MLA_OK;
 }
 
+// Graph plan: shapes and upper bounds only; the device planner fills in the splits on
+// every call. Capacity (work items the launches are sized for):
+//   uniform split_kv:  B * max(min(split_kv, cap), ceil(max_pages / 65535))
+//   proportional:      min(B * cap, 2 B + num_cus / row_blocks)   (+ B * ceil(max_pages /
+//                      65535) beyond 2^21 tokens), since sum_b floor(x_b) <= sum_b x_b and
+//                      the clamps to >= 1 add at most one split per request.
+int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_kv_len,
+                     int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+                     mla_decode_plan_s** out) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (batch < 1 || q_len < 1 || num_heads < 1 || max_kv_len < 1 || split_kv < 0 ||
+      max_split_kv < 1 || num_cus < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (batch > kMaxBatch || max_split_kv > MLA_MAX_SPLIT_KV ||
+      (int64_t)q_len * num_heads > MLA_MAX_ROWS_PER_REQUEST)
+    return MLA_ERR_UNSUPPORTED_SHAPE;
+  if (num_cus == 0) {
+    int rc = query_num_cus(&num_cus);
+    if (rc != MLA_OK) return rc;
+  }
+  const int32_t rows = q_len * num_heads;
+  int32_t tiles, nt;
+  row_blocks(rows, &tiles, &nt);
+  const int64_t max_pages = ceil_div(max_kv_len, kPage);
+  const int64_t long_split = ceil_div(max_pages, kMaxChunkPages);  // forced splits per request
+  int64_t per_req, cap;
+  if (split_kv > 0) {
+    per_req = std::max<int64_t>(std::min<int64_t>(split_kv, max_split_kv), long_split);
+    cap = (int64_t)batch * per_req;
+  } else {
+    per_req = std::max<int64_t>(max_split_kv, long_split);
+    cap = std::min<int64_t>((int64_t)batch * max_split_kv, 2LL * batch + num_cus / tiles);
+    if (long_split > 1) cap += (int64_t)batch * long_split;
+  }
+  per_req = std::min<int64_t>(per_req, max_pages);
+  cap = std::min<int64_t>(cap, (int64_t)batch * max_pages);
+  if (cap * tiles > INT32_MAX / 2 || cap >= (1 << 23)) return MLA_ERR_UNSUPPORTED_SHAPE;
+
+  auto* plan = new (std::nothrow) mla_decode_plan_s();
+  if (plan == nullptr) return MLA_ERR_NOMEM;
+  PlanDev& d = plan->dev;
+  std::memset(&d, 0, sizeof(d));
+  d.batch = batch;
+  d.q_len = q_len;
+  d.heads = num_heads;
+  d.rows = rows;
+  d.tiles = tiles;
+  d.nt = nt;
+  d.total_parts = (int32_t)cap;
+  plan->device_lengths = 1;
+  plan->max_kv_len = max_kv_len;
+  plan->split_kv = split_kv;
+  plan->max_split_kv = max_split_kv;
+  plan->kv_lens = nullptr;
+  plan->merge_groups = merge_groups_for(per_req, (int64_t)batch * rows, num_cus);
+  d.groups = plan->merge_groups;  // launch width; the device planner picks <= this
+  plan->max_splits = (int32_t)per_req;
+  plan->num_cus = num_cus;
+  plan->ws_plan_bytes = align256(sizeof(PlanDev));
+  plan->ws_o_bytes = align256((size_t)cap * rows * kDV * sizeof(float));
+  plan->ws_stats_bytes = align256((size_t)cap * rows * kStatStride * sizeof(float));
+  *out = plan;
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" {
+
+int mla_decode_plan_graph(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_kv_len,
+                          int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+                          mla_decode_plan_t** out) {
+  return mla::build_graph_plan(batch, q_len, num_heads, max_kv_len, split_kv, max_split_kv,
+                               num_cus, out);
+}
 
 int mla_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
                     int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
@@ -168,7 +249,7 @@ void mla_decode_plan_destroy(mla_decode_plan_t* plan) {
 
 size_t mla_decode_workspace_size(const mla_decode_plan_t* plan) {
   if (plan == nullptr) return 0;
-  return plan->ws_o_bytes + plan->ws_stats_bytes;
+  return plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes;
 }
 
 int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,
@@ -184,9 +265,10 @@ int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info
   info->work_items = d.total_parts * d.tiles;
   info->merge_groups = plan->merge_groups;
   info->max_splits = plan->max_splits;
-  for (int32_t b = 0; b < d.batch; ++b) {
-    if (splits) splits[b] = d.splits[b];
-    if (chunk_tokens) chunk_tokens[b] = mla::chunk_pages_of(d, b) * mla::kPage;
+  for (int32_t b = 0; b < d.batch; ++b) {  // graph plans: decided on the device, 0 here
+    if (splits) splits[b] = plan->device_lengths ? 0 : d.splits[b];
+    if (chunk_tokens)
+      chunk_tokens[b] = plan->device_lengths ? 0 : mla::chunk_pages_of(d, b) * mla::kPage;
   }
   return MLA_OK;
 }

@@ -1,0 +1,136 @@
+// Device split planner for the graph path of split-KV MLA decode.
+//
+// The same plan as the host planner (plan.cpp), computed on the GPU from the request
+// lengths in device memory, so that planning, the partial kernel and the merge can be
+// captured in one HIP graph and replayed while the lengths change. This is the setting
+// of TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA decode slower after #19338" (follow-up
+// comments: under CUDA graphs the KV lengths are not on the host, so the split plan is
+// made from device data and the kernel skips empty splits).
+//
+// One workgroup of 256 threads; thread b owns request b:
+//   L_b = clamp(kv_lens[b], 0, max_kv_len), pages_b = ceil(L_b / 32)
+//   wanted splits: the uniform bound min(split_kv, cap), or the one-wave proportional
+//   rule floor(num_cus pages_b / (row_blocks sum pages)) clamped to [1, cap]
+//   S_b = clamp(wanted, 1, max(pages_b, 1)), at least ceil(pages_b / 65535),
+//   chunk_b = ceil(pages_b / S_b) pages, S_b = ceil(pages_b / chunk_b)  (no empty split)
+// then the requests are ranked longest chunk first (ties by index, the host planner's
+// stable order) and the prefix sums of S_b give each request's first split and the
+// sorted work list. A request of length 0 gets one split with no keys (its rows come
+// out with O = 0 and LSE = -inf).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPlanThreads = 256;
+static_assert(kPlanThreads >= kMaxBatch, "one thread per request");
+
+struct PlanParams {
+  int32_t batch, q_len, heads, rows, tiles, nt;
+  int32_t max_kv_len, split_kv, max_split_kv, num_cus, cap_parts, max_groups;
+};
+
+__global__ void __launch_bounds__(kPlanThreads)
+device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
+                   PlanDev* __restrict__ out) {
+  __shared__ int64_t red[kPlanThreads];
+  __shared__ int32_t s_splits[kMaxBatch];
+  __shared__ int32_t s_chunk[kMaxBatch];
+  __shared__ int32_t s_order[kMaxBatch];
+  __shared__ int32_t s_max;
+  const int b = threadIdx.x;
+  const bool live = b < pp.batch;
+
+  int32_t L = 0;
+  if (live) L = min(max(kv_lens[b], 0), pp.max_kv_len);
+  const int64_t pages = ((int64_t)L + kPage - 1) / kPage;
+  red[b] = live ? pages : 0;
+  __syncthreads();
+  for (int w = kPlanThreads / 2; w > 0; w >>= 1) {
+    if (b < w) red[b] += red[b + w];
+    __syncthreads();
+  }
+  const int64_t total_pages = red[0];
+
+  if (live) {
+    int64_t want;
+    if (pp.split_kv > 0) {
+      want = min(pp.split_kv, pp.max_split_kv);
+    } else {
+      const double per_page = total_pages > 0
+          ? (double)pp.num_cus / ((double)pp.tiles * (double)total_pages) : 0.0;
+      want = (int64_t)(per_page * (double)pages);
+      want = max((int64_t)1, min(want, (int64_t)pp.max_split_kv));
+    }
+    int64_t s = max((int64_t)1, min(want, max(pages, (int64_t)1)));
+    s = max(s, (pages + kMaxChunkPages - 1) / kMaxChunkPages);
+    const int64_t chunk = max((int64_t)1, (pages + s - 1) / s);
+    s = max((int64_t)1, (pages + chunk - 1) / chunk);
+    s_splits[b] = (int32_t)s;
+    s_chunk[b] = (int32_t)chunk;
+    out->kv_len[b] = (uint32_t)L;
+    out->splits[b] = (uint16_t)s;
+  }
+  if (b == 0) s_max = 0;
+  __syncthreads();
+  if (live) atomicMax(&s_max, s_splits[b]);  // LDS atomic
+  if (live) {
+    int32_t base = 0, rank = 0;
+    for (int i = 0; i < pp.batch; ++i) {
+      if (i < b) base += s_splits[i];
+      if (s_chunk[i] > s_chunk[b] || (s_chunk[i] == s_chunk[b] && i < b)) ++rank;
+    }
+    out->part_base[b] = (uint32_t)base;
+    s_order[rank] = b;
+  }
+  __syncthreads();
+  if (live) {
+    uint32_t run = 0;
+    for (int e = 0; e <= b; ++e) run += (uint32_t)s_splits[s_order[e]];
+    out->sorted[b] = (run << 8) | (uint32_t)s_order[b];
+    if (b == pp.batch - 1) {
+      out->batch = pp.batch;
+      out->q_len = pp.q_len;
+      out->heads = pp.heads;
+      out->rows = pp.rows;
+      out->tiles = pp.tiles;
+      // never more work items than the launches were sized for (the host bound holds by
+      // construction; the clamp only keeps a broken bound from reading past them)
+      out->total_parts = (int32_t)min(run, (uint32_t)pp.cap_parts);
+      out->nt = pp.nt;
+      // merge width by the host planner's rule, from the actual largest split count
+      int32_t g = 1;
+      while (g * 2 <= 16 && g * 2 <= s_max) g *= 2;
+      while (g > 1 && (int64_t)pp.batch * pp.rows * g > 8LL * pp.num_cus) g /= 2;
+      out->groups = min(g, pp.max_groups);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,
+                       void* stream) {
+  const PlanDev& d = plan.dev;
+  PlanParams pp;
+  pp.batch = d.batch;
+  pp.q_len = d.q_len;
+  pp.heads = d.heads;
+  pp.rows = d.rows;
+  pp.tiles = d.tiles;
+  pp.nt = d.nt;
+  pp.max_kv_len = plan.max_kv_len;
+  pp.split_kv = plan.split_kv;
+  pp.max_split_kv = plan.max_split_kv;
+  pp.num_cus = plan.num_cus;
+  pp.cap_parts = d.total_parts;
+  pp.max_groups = plan.merge_groups;
+  hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
+                     pp, kv_lens, out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace mla

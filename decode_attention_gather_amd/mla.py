@@ -27,9 +27,10 @@ MLA_ERR_HIP_BASE = -1000
 D_QK, D_V, PAGE = 576, 512, 32
 
 EXPORTS = [
-    "mla_decode_plan", "mla_decode_plan_destroy", "mla_decode_workspace_size",
-    "mla_decode_plan_get_info", "mla_decode_partial", "mla_decode_merge",
-    "mla_decode_merge_f32", "mla_decode", "mla_decode_strerror",
+    "mla_decode_plan", "mla_decode_plan_graph", "mla_decode_plan_destroy",
+    "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_partial",
+    "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_graph",
+    "mla_decode_strerror",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -53,6 +54,10 @@ class PlanInfo(ctypes.Structure):
 
 _lib.mla_decode_plan.restype = ctypes.c_int
 _lib.mla_decode_plan.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
+_lib.mla_decode_plan_graph.restype = ctypes.c_int
+_lib.mla_decode_plan_graph.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
+_lib.mla_decode_graph.restype = ctypes.c_int
+_lib.mla_decode_graph.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _sz, _p, _p, _p]
 _lib.mla_decode_plan_destroy.restype = None
 _lib.mla_decode_plan_destroy.argtypes = [_p]
 _lib.mla_decode_workspace_size.restype = _sz
@@ -115,6 +120,23 @@ class Plan:
         self.q_len = q_len
         self.num_heads = num_heads
 
+    @classmethod
+    def graph(cls, batch: int, *, q_len: int, num_heads: int, max_kv_len: int,
+              split_kv: int = 0, max_split_kv: int = 128, num_cus: int = 0) -> "Plan":
+        """A graph plan: shapes and bounds only; the splits are planned on the device from
+        the device lengths on every decode_graph() call (capturable in a HIP graph)."""
+        self = cls.__new__(cls)
+        h = ctypes.c_void_p()
+        _check(_lib.mla_decode_plan_graph(batch, q_len, num_heads, max_kv_len, split_kv,
+                                          max_split_kv, num_cus, ctypes.byref(h)),
+               "mla_decode_plan_graph")
+        self._h = h
+        self._destroy = _lib.mla_decode_plan_destroy
+        self.batch = batch
+        self.q_len = q_len
+        self.num_heads = num_heads
+        return self
+
     @property
     def handle(self):
         return self._h
@@ -167,6 +189,21 @@ def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
                            block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
                            float(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
                            _ptr(lse), _stream(stream)), "mla_decode")
+
+
+def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, output_scale,
+                 workspace, o, lse=None, stream=None):
+    """Device-planned decode: kv_lens, softmax_scale and output_scale are device tensors
+    (int32 [B], float32 [1], float32 [1]); nothing here reads them on the host."""
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    for name, t in (("softmax_scale", softmax_scale), ("output_scale", output_scale)):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 device tensor")
+    _check(_lib.mla_decode_graph(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                 block_table.stride(0), _ptr(kv_lens), _ptr(softmax_scale),
+                                 _ptr(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
+                                 _ptr(lse), _stream(stream)), "mla_decode_graph")
 
 
 @dataclass

@@ -154,6 +154,38 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
                float softmax_scale, float output_scale, void* workspace,
                size_t workspace_bytes, void* o, float* lse, void* stream);
 
+/*
+ * Graph path (the deployment setting of issue #20510, follow-up comments: under CUDA
+ * graphs the KV lengths are not on the host, the scales come from device tensors, and
+ * the kernel skips empty splits). Everything a call does is device work on `stream`
+ * with no host read of device data, so a call can be captured in a HIP graph and
+ * replayed while kv_lens and the scales change.
+ *
+ * mla_decode_plan_graph builds a plan from shapes and bounds only:
+ *   max_kv_len    upper bound of every device length (>= 1); block-table rows must hold
+ *                 ceil(max_kv_len / 32) entries (bt_stride);
+ *   split_kv, max_split_kv, num_cus as for mla_decode_plan.
+ * The workspace it asks for (mla_decode_workspace_size) is sized for the largest plan
+ * any lengths <= max_kv_len can produce, plus the device plan at its head.
+ * mla_decode_plan_get_info reports that capacity (splits and chunk_tokens are 0).
+ *
+ * mla_decode_graph runs three kernels: the device planner (the host planner's rules,
+ * applied to kv_lens clamped to [0, max_kv_len]), the partial pass and the merge.
+ *   kv_lens        int32 [batch], device; a request with length 0 (or shorter than
+ *                  q_len, for the rows that see no key) yields O = 0 and LSE = -inf;
+ *   softmax_scale  fp32 [1], device; output_scale fp32 [1], device;
+ * other arguments as for mla_decode. Calls with a graph plan through mla_decode /
+ * _partial / _merge (and the reverse) return MLA_ERR_INVALID_ARG.
+ */
+int mla_decode_plan_graph(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_kv_len,
+                          int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+                          mla_decode_plan_t** out);
+
+int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                     const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                     const float* softmax_scale, const float* output_scale, void* workspace,
+                     size_t workspace_bytes, void* o, float* lse, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_decode_strerror(int status);
 

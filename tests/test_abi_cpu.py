@@ -170,3 +170,96 @@ def test_call_validation_before_launch():
 def test_strerror():
     for s in (0, -1, -2, -3, -4, -1001, 7):
         assert isinstance(mla.strerror(s), str) and mla.strerror(s)
+
+
+# ---- graph plans (device lengths) -----------------------------------------------------
+
+def gplan(batch, max_len, q_len=1, heads=12, split=0, cap=128, cus=256):
+    return mla.Plan.graph(batch, q_len=q_len, num_heads=heads, max_kv_len=max_len,
+                          split_kv=split, max_split_kv=cap, num_cus=cus)
+
+
+@pytest.mark.parametrize("batch,max_len,q,h,split,cap_parts", [
+    (16, 131072, 1, 12, 0, 16 * 2 + 256),        # min(B cap, 2 B + CUs / row blocks)
+    (1, 2048, 1, 12, 0, 64),                      # bounded by the pages: 2048 / 32
+    (16, 131072, 8, 12, 6, 96),                   # uniform: B * split
+    (4, 131072, 1, 12, 25, 100),
+    (8, 131072, 8, 96, 0, 8 * 2 + 256 // 8),      # 8 row blocks per split
+    (2, 100, 1, 12, 0, 8),                        # 4 pages per request at most
+    (1, 3 * 2 ** 21, 1, 12, 0, 128 + 4),          # > 2^21 tokens: + B ceil(pages / 65535)
+])
+def test_graph_plan_capacity(batch, max_len, q, h, split, cap_parts):
+    info, splits, chunk = gplan(batch, max_len, q, h, split).info()
+    assert info.total_splits == cap_parts
+    assert info.work_items == cap_parts * info.row_tiles
+    assert splits == [0] * batch and chunk == [0] * batch  # decided on the device
+    p = gplan(batch, max_len, q, h, split)
+    rows = q * h
+    head = 3840  # the device plan (PlanDev, 3616 bytes) at the workspace head, 256-aligned
+    o = (cap_parts * rows * 2048 + 255) // 256 * 256
+    st = (cap_parts * rows * 16 + 255) // 256 * 256
+    assert p.workspace_size() == head + o + st
+
+
+def test_graph_plan_capacity_covers_device_plans():
+    """Upper bound of the device planner's split counts (its rules restated here): for
+    random lengths up to the bound, sum_b S_b never exceeds the capacity."""
+    import random
+    rnd = random.Random(5)
+    for _ in range(300):
+        B = rnd.randint(1, 32)
+        max_len = rnd.choice([1, 31, 32, 100, 4096, 131072, 1 << 20])
+        split = rnd.choice([0, 0, 1, 3, 128])
+        cap = rnd.choice([1, 16, 128])
+        cus = rnd.choice([8, 80, 256])
+        heads = rnd.choice([1, 12, 96])
+        info = gplan(B, max_len, 1, heads, split, cap, cus).info()[0]
+        lens = [rnd.randint(0, max_len) for _ in range(B)]
+        hp = None
+        if min(lens) >= 1:
+            hp = mla.Plan(lens, q_len=1, num_heads=heads, split_kv=split, max_split_kv=cap,
+                          num_cus=cus).info()[0]
+            assert hp.total_splits <= info.total_splits, (B, max_len, split, cap, cus, lens)
+            assert hp.merge_groups <= info.merge_groups
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(max_len=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(q=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(split=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(batch=257), mla.MLA_ERR_UNSUPPORTED_SHAPE),
+    (dict(cap=2000), mla.MLA_ERR_UNSUPPORTED_SHAPE),
+])
+def test_graph_plan_rejects(kw, status):
+    args = dict(batch=2, max_len=100, q=1, heads=12, split=0, cap=128, cus=256)
+    args.update(kw)
+    with pytest.raises(mla.MlaError) as ei:
+        gplan(args["batch"], args["max_len"], args["q"], args["heads"], args["split"],
+              args["cap"], args["cus"])
+    assert ei.value.status == status
+
+
+def test_graph_and_host_plans_not_interchangeable():
+    lib = mla.lib_handle()
+    g = gplan(2, 100)
+    h = plan([100, 50], 1, 12, 2)
+    fake = ctypes.c_void_p(0x10000)
+    nul = None
+    need = g.workspace_size()
+    # a graph plan through the host-plan entry points
+    assert lib.mla_decode(g.handle, fake, fake, fake, 4, fake, 0.07, 1.0, fake, need, fake, nul,
+                          nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_partial(g.handle, fake, fake, fake, 4, fake, 0.07, fake, need,
+                                  nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_merge(g.handle, fake, need, 1.0, fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # a host plan through the graph entry point
+    assert lib.mla_decode_graph(h.handle, fake, fake, fake, 4, fake, fake, fake, fake,
+                                h.workspace_size(), fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # graph call validation: null scale pointers, short block-table rows, workspace
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, nul, fake, fake, need, fake,
+                                nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 3, fake, fake, fake, fake, need, fake,
+                                nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, fake, fake, fake, need - 1,
+                                fake, nul, nul) == mla.MLA_ERR_WORKSPACE
