@@ -132,11 +132,34 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
                                  output_scale, o, false, lse, stream));
 }
 
+int mla_decode_varq(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                    const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                    const int32_t* q_lens, float softmax_scale, float output_scale,
+                    void* workspace, size_t workspace_bytes, void* o, float* lse,
+                    void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if (q_lens == nullptr || !aligned(q_lens, 4)) return MLA_ERR_INVALID_ARG;
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
+                         workspace, workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  rc = check_merge(plan, workspace, workspace_bytes, output_scale, o, lse);
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                 block_table, bt_stride, kv_lens, softmax_scale,
+                                 ws_o_of(plan, workspace), ws_stats_of(plan, workspace), stream,
+                                 nullptr, q_lens));
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 output_scale, o, false, lse, stream));
+}
+
 int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
                      const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
-                     const float* softmax_scale, const float* output_scale, void* workspace,
-                     size_t workspace_bytes, void* o, float* lse, void* stream) {
+                     const int32_t* q_lens, const float* softmax_scale, const float* output_scale,
+                     void* workspace, size_t workspace_bytes, void* o, float* lse,
+                     void* stream) {
   if (plan == nullptr || !plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if (q_lens != nullptr && !aligned(q_lens, 4)) return MLA_ERR_INVALID_ARG;
   if (softmax_scale == nullptr || output_scale == nullptr || !aligned(softmax_scale, 4) ||
       !aligned(output_scale, 4))
     return MLA_ERR_INVALID_ARG;
@@ -152,7 +175,7 @@ int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* k
   if (rc != MLA_OK) return rc;
   rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache, block_table,
                                  bt_stride, kv_lens, 1.f, ws_o_of(plan, workspace),
-                                 ws_stats_of(plan, workspace), stream, &dev));
+                                 ws_stats_of(plan, workspace), stream, &dev, q_lens));
   if (rc != MLA_OK) return rc;
   return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace), 1.f,
                                  o, false, lse, stream, &dev));

@@ -87,15 +87,16 @@ struct DeviceArgs {
 
 // Launchers (defined next to their kernels). Return a hipError_t value as int. With
 // dev != nullptr the kernels read the plan and the scales from device memory and the
-// launch is sized by the plan's capacity.
+// launch is sized by the plan's capacity. q_lens (device, may be null): per-request
+// query tokens of a ragged batch, each clamped to [0, q_len].
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                   const DeviceArgs* dev = nullptr);
+                   const DeviceArgs* dev = nullptr, const int32_t* q_lens = nullptr);
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev);
+                        const DeviceArgs* dev, const int32_t* q_lens);
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
                  const DeviceArgs* dev = nullptr);

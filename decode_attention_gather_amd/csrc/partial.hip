@@ -129,8 +129,11 @@ struct Item {
   float* ws_stats;
   float scale_log2;
   int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int qb;  // query tokens of the request (ragged batches), <= q_len
   int lane, w, g, l16;
 };
+
+constexpr int kNoKey = -0x40000000;  // causal limit of a row that sees no key
 
 // One wave's whole life: prologue, then 1 + nsteps barriers like every other wave.
 template <int NT, bool kDoQK, bool kDoLd, bool kDoPV>
@@ -165,10 +168,15 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
     if (!qrow_valid || g >= 2) { a = 0; c = 0; }
     qf[kDoQK ? 4 : 0] = cat8(a, c);
     // causal limit of the row: query j sees tokens < L - q_len + j + 1
-    const int jq = qrow_valid ? qrow / P.heads : P.q_len - 1;
-    lim_q = min(t1, L - P.q_len + jq + 1);
+    // causal limit of the row: query j of a request with qb queries sees tokens
+    // < L - qb + j + 1; rows past the request's queries see none
+    const int qb = it.qb;
+    const int jq = qrow_valid ? qrow / P.heads : 0;
+    lim_q = jq < qb ? min(t1, L - qb + jq + 1) : kNoKey;
     // below this token no row of the work item needs a mask
-    lim_all = min(t1, L - P.q_len + min(row0, P.rows - 1) / P.heads + 1);
+    const int j_first = min(row0, P.rows - 1) / P.heads;
+    const int j_last = (min(row0 + NT * kTileRows, P.rows) - 1) / P.heads;
+    lim_all = j_last >= qb ? kNoKey : min(t1, L - qb + j_first + 1);
     // K operand: token row n = 16 tt + l16 of the page, bytes 128 c4 + 32 g (+16)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -448,8 +456,8 @@ __global__ void __launch_bounds__(Roles<NT>::kThreads, 1)
 partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt, int64_t bt_stride,
-               const int32_t* __restrict__ kv_lens, float scale_log2_arg,
-               float* __restrict__ ws_o, float* __restrict__ ws_stats) {
+               const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ q_lens,
+               float scale_log2_arg, float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ Smem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
   const float scale_log2 = kDev ? *scale_dev * 1.4426950408889634f : scale_log2_arg;
@@ -481,6 +489,7 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.b = b;
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
+  it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
   const int chunk_tok = chunk_pages_of(P, b) * kPage;
   const int t0 = s * chunk_tok;
   it.t1 = max(t0, min(t0 + chunk_tok, it.L));
@@ -501,11 +510,11 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                   const DeviceArgs* dev) {
+                   const DeviceArgs* dev, const int32_t* q_lens) {
   const PlanDev& P = plan.dev;
   if (P.nt > kMaxTilesPerBlock)
     return launch_partial_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
-                               stream, dev);
+                               stream, dev, q_lens);
   const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -514,14 +523,14 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   hipStream_t st = (hipStream_t)stream;
   if (P.nt == 1) {
     if (dev)
-      hipLaunchKernelGGL((partial_kernel<1, true>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<1, true>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_kernel<1, false>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<1, false>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
   } else {
     if (dev)
-      hipLaunchKernelGGL((partial_kernel<2, true>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<2, true>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_kernel<2, false>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<2, false>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

@@ -177,8 +177,11 @@ struct WItem {
   float* ws_stats;
   float scale_log2;
   int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int qb;  // query tokens of the request (ragged batches), <= q_len
   int lane, w, g, l16;
 };
+
+constexpr int kNoKey = -0x40000000;  // causal limit of a row that sees no key
 
 // ------------------------------------------------------------------ QK waves
 // QK wave qw: S^T = K Q^T of both pages of a step for row tiles qw NT/2 + k, the
@@ -214,13 +217,16 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
     // rope: two K = 32 steps, lane group g holds bytes [8 g, 8 g + 8) of each half
     qr[k][0] = valid ? *(const long*)(qp + 512 + 8 * g) : 0;
     qr[k][1] = valid ? *(const long*)(qp + 544 + 8 * g) : 0;
-    // causal limit of the row: query j sees tokens < L - q_len + j + 1
-    const int jq = valid ? qrow / P.heads : P.q_len - 1;
-    lim_q[k] = min(t1, it.L - P.q_len + jq + 1);
+    // causal limit of the row: query j of a request with qb queries sees tokens
+    // < L - qb + j + 1; rows past the request's queries see none
+    const int jq = valid ? qrow / P.heads : 0;
+    lim_q[k] = jq < it.qb ? min(t1, it.L - it.qb + jq + 1) : kNoKey;
   }
   // below this token no row of the wave needs a mask
   const int first_row = min(it.row0 + qw * kT * kTileRows, P.rows - 1);
-  const int lim_all = min(t1, it.L - P.q_len + first_row / P.heads + 1);
+  const int last_row = min(it.row0 + (qw + 1) * kT * kTileRows, P.rows) - 1;
+  const int lim_all = last_row / P.heads >= it.qb
+      ? kNoKey : min(t1, it.L - it.qb + first_row / P.heads + 1);
 
   // K operand offsets inside a token row (swizzled chunks; rot depends on l16 only).
   const int rot = l16 >> 2;
@@ -511,7 +517,8 @@ __global__ void __launch_bounds__(WRoles<NT>::kThreads, 1)
 partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                     const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                     const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt,
-                    int64_t bt_stride, const int32_t* __restrict__ kv_lens, float scale_log2_arg,
+                    int64_t bt_stride, const int32_t* __restrict__ kv_lens,
+                    const int32_t* __restrict__ q_lens, float scale_log2_arg,
                     float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ WSmem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
@@ -544,6 +551,7 @@ partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.b = b;
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
+  it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
   const int chunk_tok = chunk_pages_of(P, b) * kPage;
   const int t0 = s * chunk_tok;
   it.t1 = max(t0, min(t0 + chunk_tok, it.L));
@@ -561,7 +569,7 @@ partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev) {
+                        const DeviceArgs* dev, const int32_t* q_lens) {
   const PlanDev& P = plan.dev;
   const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
@@ -572,17 +580,17 @@ int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const u
   if (P.nt == 4) {
     if (dev)
       hipLaunchKernelGGL((partial_wide_kernel<4, true>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
     else
       hipLaunchKernelGGL((partial_wide_kernel<4, false>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
   } else {
     if (dev)
       hipLaunchKernelGGL((partial_wide_kernel<6, true>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
     else
       hipLaunchKernelGGL((partial_wide_kernel<6, false>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

@@ -29,8 +29,8 @@ D_QK, D_V, PAGE = 576, 512, 32
 EXPORTS = [
     "mla_decode_plan", "mla_decode_plan_graph", "mla_decode_plan_destroy",
     "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_partial",
-    "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_graph",
-    "mla_decode_strerror",
+    "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
+    "mla_decode_graph", "mla_decode_strerror",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -57,7 +57,9 @@ _lib.mla_decode_plan.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.
 _lib.mla_decode_plan_graph.restype = ctypes.c_int
 _lib.mla_decode_plan_graph.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
 _lib.mla_decode_graph.restype = ctypes.c_int
-_lib.mla_decode_graph.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _sz, _p, _p, _p]
+_lib.mla_decode_graph.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _sz, _p, _p, _p]
+_lib.mla_decode_varq.restype = ctypes.c_int
+_lib.mla_decode_varq.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _f32, _f32, _p, _sz, _p, _p, _p]
 _lib.mla_decode_plan_destroy.restype = None
 _lib.mla_decode_plan_destroy.argtypes = [_p]
 _lib.mla_decode_workspace_size.restype = _sz
@@ -182,9 +184,17 @@ def merge(plan: Plan, workspace, output_scale: float, o, lse=None, stream=None):
 
 
 def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
-           output_scale: float, workspace, o, lse=None, stream=None):
+           output_scale: float, workspace, o, lse=None, stream=None, q_lens=None):
+    """q_lens (device int32 [B], optional): a ragged batch (mla_decode_varq)."""
     if o.dtype != torch.bfloat16:
         raise TypeError("o must be bfloat16")
+    if q_lens is not None:
+        _check(_lib.mla_decode_varq(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                    block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                    float(softmax_scale), float(output_scale), _ptr(workspace),
+                                    workspace.numel(), _ptr(o), _ptr(lse), _stream(stream)),
+               "mla_decode_varq")
+        return
     _check(_lib.mla_decode(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
                            block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
                            float(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
@@ -192,7 +202,7 @@ def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
 
 
 def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, output_scale,
-                 workspace, o, lse=None, stream=None):
+                 workspace, o, lse=None, stream=None, q_lens=None):
     """Device-planned decode: kv_lens, softmax_scale and output_scale are device tensors
     (int32 [B], float32 [1], float32 [1]); nothing here reads them on the host."""
     if o.dtype != torch.bfloat16:
@@ -201,7 +211,8 @@ def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, o
         if t.dtype != torch.float32 or not t.is_cuda:
             raise TypeError(f"{name} must be a float32 device tensor")
     _check(_lib.mla_decode_graph(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
-                                 block_table.stride(0), _ptr(kv_lens), _ptr(softmax_scale),
+                                 block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                 _ptr(softmax_scale),
                                  _ptr(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
                                  _ptr(lse), _stream(stream)), "mla_decode_graph")
 

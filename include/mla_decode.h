@@ -155,6 +155,20 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
                size_t workspace_bytes, void* o, float* lse, void* stream);
 
 /*
+ * Ragged query batch (the module's is_var_q / query_lens in issue #20510, Repro 1):
+ * as mla_decode with a plan built for q_len = the largest query count, plus
+ *   q_lens  device int32 [batch]: query tokens of request b (clamped to [0, q_len]).
+ * q, o and lse keep the [B][q_len][H] layout; query j < q_lens[b] of request b sees
+ * keys [0, L_b - q_lens[b] + j] (the causal MTP rule with that request's count), and
+ * rows j >= q_lens[b] come out as O = 0, LSE = -inf.
+ */
+int mla_decode_varq(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                    const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                    const int32_t* q_lens, float softmax_scale, float output_scale,
+                    void* workspace, size_t workspace_bytes, void* o, float* lse,
+                    void* stream);
+
+/*
  * Graph path (the deployment setting of issue #20510, follow-up comments: under CUDA
  * graphs the KV lengths are not on the host, the scales come from device tensors, and
  * the kernel skips empty splits). Everything a call does is device work on `stream`
@@ -173,6 +187,7 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
  * applied to kv_lens clamped to [0, max_kv_len]), the partial pass and the merge.
  *   kv_lens        int32 [batch], device; a request with length 0 (or shorter than
  *                  q_len, for the rows that see no key) yields O = 0 and LSE = -inf;
+ *   q_lens         int32 [batch], device, or NULL: a ragged batch as in mla_decode_varq;
  *   softmax_scale  fp32 [1], device; output_scale fp32 [1], device;
  * other arguments as for mla_decode. Calls with a graph plan through mla_decode /
  * _partial / _merge (and the reverse) return MLA_ERR_INVALID_ARG.
@@ -183,8 +198,9 @@ int mla_decode_plan_graph(int32_t batch, int32_t q_len, int32_t num_heads, int32
 
 int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
                      const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
-                     const float* softmax_scale, const float* output_scale, void* workspace,
-                     size_t workspace_bytes, void* o, float* lse, void* stream);
+                     const int32_t* q_lens, const float* softmax_scale,
+                     const float* output_scale, void* workspace, size_t workspace_bytes,
+                     void* o, float* lse, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_decode_strerror(int status);

@@ -254,12 +254,20 @@ def test_graph_and_host_plans_not_interchangeable():
                                   nul) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_decode_merge(g.handle, fake, need, 1.0, fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
     # a host plan through the graph entry point
-    assert lib.mla_decode_graph(h.handle, fake, fake, fake, 4, fake, fake, fake, fake,
+    assert lib.mla_decode_graph(h.handle, fake, fake, fake, 4, fake, nul, fake, fake, fake,
                                 h.workspace_size(), fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
-    # graph call validation: null scale pointers, short block-table rows, workspace
-    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, nul, fake, fake, need, fake,
-                                nul, nul) == mla.MLA_ERR_INVALID_ARG
-    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 3, fake, fake, fake, fake, need, fake,
-                                nul, nul) == mla.MLA_ERR_INVALID_ARG
-    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, fake, fake, fake, need - 1,
-                                fake, nul, nul) == mla.MLA_ERR_WORKSPACE
+    # graph call validation: null scale pointers, short block-table rows, workspace,
+    # misaligned q_lens
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, nul, nul, fake, fake, need,
+                                fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 3, fake, nul, fake, fake, fake, need,
+                                fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, nul, fake, fake, fake,
+                                need - 1, fake, nul, nul) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_graph(g.handle, fake, fake, fake, 4, fake, ctypes.c_void_p(0x10002),
+                                fake, fake, fake, need, fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # ragged-query entry point: needs q_lens, refuses graph plans
+    assert lib.mla_decode_varq(h.handle, fake, fake, fake, 4, fake, nul, 0.07, 1.0, fake,
+                               h.workspace_size(), fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_varq(g.handle, fake, fake, fake, 4, fake, fake, 0.07, 1.0, fake, need,
+                               fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
