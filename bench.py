@@ -157,6 +157,29 @@ def bench_plan(mla, dc, q, rows, kv_bytes, kv_lens, split_kv, steps, warmup, col
     return res
 
 
+def graph_path(mla, dc, q, rows, kv_bytes, steps, warmup):
+    """Times the graph-capturable call (device planner + partial + merge, device lengths
+    and scales) with the plan's length bound at the batch's longest request."""
+    lens = dc.kv_lens_host
+    plan = mla.Plan.graph(len(lens), q_len=q.shape[1], num_heads=q.shape[2],
+                          max_kv_len=max(lens))
+    ws = plan.alloc_workspace()
+    o = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    ss = torch.tensor([dc.softmax_scale], dtype=torch.float32, device="cuda")
+    os_ = torch.tensor([dc.output_scale], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        mla.decode_graph(plan, q, dc.kv, dc.block_table, dc.kv_lens, ss, os_, ws, o, lse, stream)
+
+    us, per, _ = time_steps(call, steps, warmup, stream)
+    info = plan.info()[0]
+    plan.close()
+    return dict(us_per_call=round(us, 2), call=stats(per), work_item_capacity=info.work_items,
+                kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1))
+
+
 def q8_sibling(case, q_len=8, seed=20263):
     """Queries for the q = 8 sibling of a workload: N(0, 1) E4M3 rows drawn from their
     own seeded generator, used with the workload's KV cache and block table."""
@@ -246,6 +269,8 @@ def bench_other(mla, name, steps, warmup):
         out.append(r)
     if name.startswith("c1_"):
         out[-1]["graph"] = graph_timing(mla, dc, c)
+    if name.startswith("s_"):
+        out[-1]["graph_path"] = graph_path(mla, dc, dc.q, c.rows, by["kv"], steps, warmup)
     del dc
     torch.cuda.empty_cache()
     return out
@@ -299,6 +324,8 @@ def main():
     native = bench_plan(mla, dc, dc.q, case.rows, by["kv"], dc.kv_lens_host, 0, steps, warmup,
                         cold_calls=20)
     print(f"[bench] planner plan: {native['us_per_call']} us/call", file=sys.stderr, flush=True)
+    gpath = graph_path(mla, dc, dc.q, case.rows, by["kv"], steps, warmup)
+    print(f"[bench] graph path: {gpath['us_per_call']} us/call", file=sys.stderr, flush=True)
 
     q8 = None
     if not args.no_q8 and name == HEADLINE:
@@ -351,6 +378,7 @@ def main():
         "fixed_split": None if fixed is None else {
             k: fixed[k] for k in ("split_kv", "us_per_call", "call", "kv_gbs", "partial_us",
                                   "work_items")},
+        "graph_path": gpath,
         "q8": q8,
         "roofline": {"bound": "hbm", "kernel": "partial_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -137,6 +137,10 @@ CONFIGS = {
                                num_heads=96, q_len=8, split_kv=0, seed=20265),
     "m_b16_h12_q1_128k": dict(kv_lens=[131072] * 16, num_heads=12, q_len=1, split_kv=6,
                               seed=20266),
+    # skewed batch: one 1M-token request beside seven short ones, H12 q8 (split planning
+    # matters most here)
+    "s_b8_h12_q8_skewed": dict(kv_lens=[1048576] + [4096] * 7, num_heads=12, q_len=8,
+                               split_kv=0, seed=20267),
 }
 
 
