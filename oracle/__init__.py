@@ -57,6 +57,15 @@ def _load(path: str | None = None):
             p, p, p, p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, ctypes.c_int64, p, p,
             ctypes.c_int]
+        lib.oracle_mla_decode_rows_ex.restype = ctypes.c_int
+        lib.oracle_mla_decode_rows_ex.argtypes = [
+            p, p, p, p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, p, ctypes.c_int64, p, p,
+            ctypes.c_int]
+        lib.oracle_round_bf16.restype = None
+        lib.oracle_round_bf16.argtypes = [p, ctypes.c_int64, p]
+        lib.oracle_mxfp8_quantize.restype = ctypes.c_int
+        lib.oracle_mxfp8_quantize.argtypes = [p, ctypes.c_int64, p, p]
         _libs[key] = lib
     return _libs[key]
 
@@ -85,13 +94,14 @@ def _np(x, dtype):
 
 def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
                softmax_scale: float, output_scale: float = 1.0, rows=None,
-               nthreads: int = 0, lib_path: str | None = None):
+               nthreads: int = 0, lib_path: str | None = None, sinks=None):
     """Return (O fp64 [nrows, 512], LSE fp64 [nrows]).
 
     q: uint8 E4M3 codes [B, q_len, H, 576]; kv_cache: uint8 [P, 32, 576];
     block_table: int32 [B, stride]; kv_lens: int32 [B]. ``rows`` lists flat row ids
     r = (b*q_len + j)*H + h (None: every row in order). The scales are used as given
-    (pass the fp32-rounded value when the GPU side takes fp32).
+    (pass the fp32-rounded value when the GPU side takes fp32). ``sinks``: per-head
+    sink logits [H] (None: no sink), in the units of the scaled scores.
     """
     lib = _load(lib_path)
     qa = _np(q, np.uint8)
@@ -114,10 +124,40 @@ def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
         rows_ptr = rows_arr.ctypes.data
     o = np.empty((nrows, D_V), dtype=np.float64)
     lse = np.empty((nrows,), dtype=np.float64)
-    rc = lib.oracle_mla_decode_rows(
-        qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
-        num_heads, stride, num_pages, float(softmax_scale), float(output_scale), rows_ptr,
-        nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if sinks is None:
+        rc = lib.oracle_mla_decode_rows(
+            qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
+            num_heads, stride, num_pages, float(softmax_scale), float(output_scale), rows_ptr,
+            nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
+    else:
+        sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float64).reshape(-1))
+        assert sk.size == num_heads, "one sink per head"
+        rc = lib.oracle_mla_decode_rows_ex(
+            qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
+            num_heads, stride, num_pages, float(softmax_scale), float(output_scale),
+            sk.ctypes.data, rows_ptr, nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_mla_decode_rows failed with code {rc}")
     return o, lse
+
+
+def round_bf16(x, lib_path: str | None = None) -> np.ndarray:
+    """fp64 array of the BF16 values nearest to x (ties to even)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty_like(a)
+    _load(lib_path).oracle_round_bf16(a.ctypes.data, a.size, out.ctypes.data)
+    return out
+
+
+def mxfp8_quantize(x, lib_path: str | None = None):
+    """MXFP8 form of rows of 512 BF16 values: (codes uint8 [n, 512], E8M0 scales uint8
+    [n, 16]), one scale per 32 consecutive elements."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(-1, D_V))
+    n = a.shape[0]
+    codes = np.empty((n, D_V), dtype=np.uint8)
+    scales = np.empty((n, D_V // 32), dtype=np.uint8)
+    rc = _load(lib_path).oracle_mxfp8_quantize(a.ctypes.data, n, codes.ctypes.data,
+                                               scales.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp8_quantize failed with code {rc}")
+    return codes, scales

@@ -43,6 +43,24 @@
  * Row order: flat row id r = (b * q_len + j) * H + h, the layout of q [B][q_len][H][576]
  * and of O [B][q_len][H][512].
  *
+ * Attention sinks [the same PR, Description: the reduction applies sinks after the
+ * combine]: the pages name sinks without a formula; this oracle takes the usual form,
+ * one extra logit sigma_h per head that joins the softmax denominator only:
+ *     m = max(max_i s_i, sigma_h),  l = sum_i exp(s_i - m) + exp(sigma_h - m)
+ *     O_d = output_scale * sum_i exp(s_i - m) V_{i,d} / l,   LSE = m + ln(l)
+ * so LSE is the log of the whole denominator and O_d = sum_i exp(s_i - LSE) V_{i,d}.
+ * sigma_h = -inf gives back the definition without a sink.
+ *
+ * MXFP8 output [TensorRT-LLM PR #17441 "m3 decode perf clean", the commit messages on
+ * the MXFP8 quantize-tile epilogue and the sparse decode merge: the merge emits E4M3
+ * values with UE8M0 block scales next to the BF16 O it stores, bit-identical to
+ * quantizing that BF16 tensor afterwards]: blocks of 32 consecutive elements of a row; the block's
+ * scale is amax / 448 rounded up to a power of two 2^e (the smallest integer e with
+ * amax <= 448 * 2^e), clamped to the E8M0 range [-127, 127] and stored as e + 127; each
+ * element is the E4M3 value nearest to x / 2^e, ties to the even code, with the sign
+ * of x. Here e is found exactly; the pages' implementation reaches it through an
+ * approximate reciprocal of 448, which can give e + 1 when amax is 1.75 * 2^k.
+ *
  * Threads: rows are handed out to POSIX threads through an atomic counter; each row's
  * arithmetic is sequential and independent of the thread count.
  */
@@ -84,6 +102,7 @@ typedef struct {
   int32_t batch, q_len, heads;
   int64_t bt_stride, num_pages;
   double softmax_scale, output_scale;
+  const double* sinks; /* [heads] extra logits, or NULL */
   const int64_t* rows;
   int64_t nrows;
   double* out_o;
@@ -126,9 +145,12 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
     s[i] = J->softmax_scale * dot;
     if (s[i] > m) m = s[i];
   }
+  /* a sink logit joins the max and, below, the normaliser */
+  double sigma = J->sinks ? J->sinks[r % J->heads] : -INFINITY;
+  if (sigma > m) m = sigma;
   /* weights, normaliser, and the weighted sum of V (the first 512 bytes of each row) */
   for (int d = 0; d < ORACLE_D_V; ++d) acc[d] = 0.0;
-  double l = 0.0;
+  double l = J->sinks ? exp(sigma - m) : 0.0;
   for (int64_t i = 0; i < n; ++i) {
     int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
     const uint8_t* v = J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;
@@ -186,14 +208,16 @@ static void* worker(void* arg) {
  *   kv      uint8 E4M3 [num_pages][32][576]
  *   bt      int32 [B][bt_stride], page indices into kv
  *   kv_lens int32 [B], each >= q_len
+ * sinks   fp64 [H] sink logits (see the header), or NULL for none
  * nthreads <= 0 uses every online core. Returns 0 or a negative error code; on error
  * the outputs are unspecified.
  */
-int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
-                           const int32_t* kv_lens, int32_t batch, int32_t q_len,
-                           int32_t num_heads, int64_t bt_stride, int64_t num_pages,
-                           double softmax_scale, double output_scale, const int64_t* rows,
-                           int64_t nrows, double* out_o, double* out_lse, int nthreads) {
+int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
+                              const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                              int32_t num_heads, int64_t bt_stride, int64_t num_pages,
+                              double softmax_scale, double output_scale, const double* sinks,
+                              const int64_t* rows, int64_t nrows, double* out_o,
+                              double* out_lse, int nthreads) {
   if (!q || !kv || !bt || !kv_lens || !out_o || !out_lse) return ORACLE_ERR_ARG;
   if (batch < 1 || q_len < 1 || num_heads < 1 || bt_stride < 1 || num_pages < 1 || nrows < 0)
     return ORACLE_ERR_ARG;
@@ -210,6 +234,7 @@ int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* b
   J->num_pages = num_pages;
   J->softmax_scale = softmax_scale;
   J->output_scale = output_scale;
+  J->sinks = sinks;
   J->rows = rows;
   J->nrows = nrows;
   J->out_o = out_o;
@@ -229,4 +254,78 @@ int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* b
   int rc = J->error;
   free(J);
   return rc;
+}
+
+/* The same without sinks. */
+int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
+                           const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                           int32_t num_heads, int64_t bt_stride, int64_t num_pages,
+                           double softmax_scale, double output_scale, const int64_t* rows,
+                           int64_t nrows, double* out_o, double* out_lse, int nthreads) {
+  return oracle_mla_decode_rows_ex(q, kv, bt, kv_lens, batch, q_len, num_heads, bt_stride,
+                                   num_pages, softmax_scale, output_scale, NULL, rows, nrows,
+                                   out_o, out_lse, nthreads);
+}
+
+/*
+ * Round each x[i] to the nearest BF16 value (8 significant bits, fp32's exponent range,
+ * subnormals down to 2^-133), ties to even; magnitudes that round past the largest
+ * finite BF16 value become infinities. NaN stays NaN.
+ */
+void oracle_round_bf16(const double* x, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    double v = x[i];
+    if (v == 0.0 || isnan(v) || isinf(v)) {
+      out[i] = v;
+      continue;
+    }
+    int k;
+    frexp(v, &k);               /* |v| in [2^(k-1), 2^k) */
+    int e = k - 1;              /* floor(log2 |v|) */
+    if (e < -126) e = -126;     /* subnormal range: fixed quantum */
+    double quantum = ldexp(1.0, e - 7);
+    double r = nearbyint(v / quantum) * quantum; /* default rounding: to nearest even */
+    if (fabs(r) >= ldexp(1.0, 128)) r = v > 0 ? INFINITY : -INFINITY;
+    out[i] = r;
+  }
+}
+
+/* The E4M3 code nearest to y (|y| <= 448), ties to the even code, sign of y kept. */
+static uint8_t e4m3_nearest(double y) {
+  double a = fabs(y);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double err = fabs(oracle_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/*
+ * MXFP8 quantization of nrows rows of 512 values (each already a BF16 value): codes
+ * uint8 E4M3 [nrows][512], scales uint8 E8M0 [nrows][16] (one per 32 consecutive
+ * elements, biased by 127). Returns 0, or ORACLE_ERR_ARG for a non-finite input.
+ */
+int oracle_mxfp8_quantize(const double* x, int64_t nrows, uint8_t* codes, uint8_t* scales) {
+  const int block = 32;
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int blk = 0; blk < ORACLE_D_V / block; ++blk) {
+      const double* xb = x + r * ORACLE_D_V + blk * block;
+      double amax = 0.0;
+      for (int i = 0; i < block; ++i) {
+        if (!isfinite(xb[i])) return ORACLE_ERR_ARG;
+        if (fabs(xb[i]) > amax) amax = fabs(xb[i]);
+      }
+      int e = -127;
+      while (e < 127 && amax > ldexp(448.0, e)) ++e;
+      scales[r * (ORACLE_D_V / block) + blk] = (uint8_t)(e + 127);
+      for (int i = 0; i < block; ++i)
+        codes[r * ORACLE_D_V + blk * block + i] = e4m3_nearest(ldexp(xb[i], -e));
+    }
+  }
+  return 0;
 }

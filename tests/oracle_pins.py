@@ -35,7 +35,7 @@ def _run(case, lib_path, rows=None, **kw):
                              q_len=case.q_len, num_heads=case.num_heads,
                              softmax_scale=kw.get("softmax_scale", F32_SCALE),
                              output_scale=kw.get("output_scale", case.output_scale),
-                             rows=rows, lib_path=lib_path)
+                             rows=rows, lib_path=lib_path, sinks=kw.get("sinks"))
 
 
 def _gather(case, b, n):
@@ -220,6 +220,151 @@ def pin_bounds_and_dominant(lib_path=None):
     np.testing.assert_allclose(o[0], v123, rtol=0, atol=1e-6)
 
 
+# ---- attention sinks: one extra logit per head in the softmax denominator --------------
+
+def pin_sinks_equal_scores(lib_path=None):
+    """softmax_scale = 0 makes every score 0; with sink sigma the closed forms are
+    O = output_scale * sum(V) / (n + e^sigma) and LSE = ln(n + e^sigma)."""
+    case = inputs.make_case([40, 7], num_heads=2, q_len=1, seed=21, output_scale=1.25)
+    for sig in (-2.0, 0.0, 3.5, 40.0):
+        sinks = [sig, sig - 1.0]
+        o, lse = _run(case, lib_path, softmax_scale=0.0, sinks=sinks)
+        for b in range(case.batch):
+            n = int(case.kv_lens[b])
+            vsum = _dec(_gather(case, b, n)[:, :inputs.D_V]).sum(dim=0).numpy()
+            for h in range(2):
+                r = b * 2 + h
+                denom = n + math.exp(sinks[h])
+                ref_o = 1.25 * vsum / denom
+                np.testing.assert_allclose(o[r], ref_o, rtol=1e-13,
+                                           atol=1e-13 * np.abs(ref_o).max())
+                ref = math.log(denom)
+                assert abs(lse[r] - ref) <= 1e-14 * max(1.0, abs(ref)), (sig, h, lse[r], ref)
+
+
+def pin_sinks_logaddexp(lib_path=None):
+    """Against the sink-free oracle: LSE_sink = logaddexp(LSE, sigma_h) and
+    O_sink = O * exp(LSE - LSE_sink), per head, up to a sink far above every score
+    (sigma = 1000, where exp(sigma) alone overflows fp64); sigma = -inf changes no bit."""
+    case = inputs.make_case([150, 33, 64], num_heads=5, q_len=2, seed=22)
+    o0, l0 = _run(case, lib_path)
+    sinks = np.array([-1.0, 2.0, 5.0, 30.0, 1000.0])
+    o1, l1 = _run(case, lib_path, sinks=sinks)
+    h = np.arange(o0.shape[0]) % case.num_heads
+    ref_l = np.logaddexp(l0, sinks[h])
+    np.testing.assert_allclose(l1, ref_l, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o1, o0 * np.exp(l0 - ref_l)[:, None], rtol=1e-11, atol=1e-15)
+    o2, l2 = _run(case, lib_path, sinks=np.full(case.num_heads, -np.inf))
+    assert np.array_equal(o2, o0) and np.array_equal(l2, l0)
+
+
+def pin_sinks_mpmath(lib_path=None):
+    """Tiny inputs with sinks against 50-digit arithmetic, no max subtraction."""
+    import mpmath
+    mpmath.mp.dps = 50
+    case = inputs.make_case([5, 3], num_heads=2, q_len=1, seed=23)
+    sinks = [0.75, -3.0]
+    o, lse = _run(case, lib_path, sinks=sinks)
+    sc = mpmath.mpf(F32_SCALE)
+    for b in range(case.batch):
+        n = int(case.kv_lens[b])
+        rows = _dec(_gather(case, b, n)).tolist()
+        for h in range(2):
+            r = b * 2 + h
+            qv = _dec(case.q[b, 0, h]).tolist()
+            es = [mpmath.exp(sc * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c)
+                                               for a, c in zip(qv, rows[i]))) for i in range(n)]
+            tot = mpmath.fsum(es) + mpmath.exp(mpmath.mpf(sinks[h]))
+            ref_lse = float(mpmath.log(tot))
+            assert abs(lse[r] - ref_lse) <= 1e-13 * max(1.0, abs(ref_lse))
+            for d in range(0, inputs.D_V, 11):
+                ref = float(mpmath.fsum(es[i] * rows[i][d] for i in range(n)) / tot)
+                assert abs(o[r, d] - ref) <= 1e-13 * max(1.0, abs(ref)), (d, o[r, d], ref)
+
+
+# ---- BF16 rounding and the MXFP8 output form ----------------------------------------
+
+def _bf16_grid_values(seed):
+    """fp32-exact test values across the BF16 range: random, exact ties (halfway
+    between BF16 neighbours), subnormals, and values that overflow."""
+    g = np.random.default_rng(seed)
+    mant = g.integers(0, 1 << 16, size=4000).astype(np.float64)
+    expo = g.integers(-140, 120, size=4000)
+    rnd = np.ldexp(1.0 + mant / 65536.0, expo) * np.where(g.random(4000) < 0.5, -1, 1)
+    # halfway points: BF16 value + half a step (odd and even neighbours)
+    base = np.ldexp(1.0 + np.arange(128) / 128.0, 3)
+    ties = np.concatenate([base + 2.0 ** -5, -(base + 2.0 ** -5)])
+    sub = np.ldexp(np.arange(1, 64, dtype=np.float64), -140)  # BF16 subnormal range
+    big = np.array([3.3895313892515355e38, 3.39e38, -3.4e38])
+    return np.concatenate([rnd, ties, sub, big]).astype(np.float32).astype(np.float64)
+
+
+def pin_bf16_rounding(lib_path=None):
+    """The oracle's BF16 rounding against torch's float -> bfloat16 cast (a separate
+    library routine) on fp32-exact values, ties and subnormals included."""
+    x = _bf16_grid_values(31)
+    ours = oracle.round_bf16(x, lib_path)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref), np.flatnonzero(ours != ref)[:5]
+    assert oracle.round_bf16([1.0 + 2.0 ** -8], lib_path)[0] == 1.0        # tie -> even
+    assert oracle.round_bf16([1.0 + 3 * 2.0 ** -8], lib_path)[0] == 1.0 + 2.0 ** -6
+
+
+def _mx_blocks(seed):
+    """Rows of BF16 values whose 32-element blocks span the interesting cases."""
+    g = np.random.default_rng(seed)
+    rows = []
+    for k in (-140, -130, -20, -3, 0, 5, 9, 40, 119):
+        x = g.standard_normal(512) * 2.0 ** k
+        rows.append(x)
+    x = np.zeros(512)
+    x[0:32] = 448.0                                   # amax exactly 448 * 2^0
+    x[32:64] = 448.0 * 2.0 ** 5                        # 448 * 2^5
+    x[64] = 448.0 * (1 + 2.0 ** -7)                    # next BF16 above 448
+    x[96] = 1.75                                      # 448 * 2^-8
+    x[128] = 1.875                                    # just above: one exponent up
+    x[160:192] = -g.random(32) * 3.0                  # negative block
+    x[192:224] = 0.0                                  # all zero
+    x[224] = -0.0
+    x[256:288] = np.ldexp(1.0 + np.arange(32) / 8.0, -3)
+    rows.append(x)
+    return oracle.round_bf16(np.stack(rows))
+
+
+def pin_mxfp8(lib_path=None):
+    """MXFP8 of BF16 rows: every scale is the smallest power of two 2^e with
+    amax <= 448 * 2^e (from frexp, a different route), clamped to [-127, 127]; every
+    element is torch's RNE float8_e4m3fn cast of x / 2^e; hand cases pin the edges."""
+    x = _mx_blocks(41)
+    codes, scales = oracle.mxfp8_quantize(x, lib_path)
+    xb = x.reshape(x.shape[0], 16, 32)
+    amax = np.abs(xb).max(axis=2)
+    # frexp: amax = f * 2^k with f in [0.5, 1); 448 = 0.875 * 2^9
+    f, k = np.frexp(amax)
+    e_ref = np.where(f <= 0.875, k - 9, k - 8)
+    e_ref = np.where(amax == 0, -127, np.clip(e_ref, -127, 127))
+    assert np.array_equal(scales.astype(np.int64) - 127, e_ref), "block scales"
+    y = xb / np.ldexp(1.0, e_ref)[:, :, None]
+    ref = torch.from_numpy(y.reshape(x.shape).astype(np.float32)).to(torch.float8_e4m3fn)
+    ref = ref.view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref), np.argwhere(codes != ref)[:5]
+    last = codes[-1]
+    assert scales[-1, 0] == 127 and (last[0:32] == 0x7E).all()       # 448 -> code 0x7E
+    assert scales[-1, 1] == 132 and (last[32:64] == 0x7E).all()
+    assert scales[-1, 2] == 128 and last[64] == 0x76                 # 452 / 2 = 226 -> 224
+    assert scales[-1, 3] == 119 and last[96] == 0x7E                 # 1.75 = 448 * 2^-8
+    assert scales[-1, 4] == 120                                      # 1.875 > 1.75
+    assert scales[-1, 6] == 0 and (last[192:224] == 0).all()         # zero block: e = -127
+    assert last[224] == 0x80                                         # -0 keeps its sign
+    # dequantization error: at most half an E4M3 step of x / 2^e
+    deq = oracle.e4m3_table(lib_path)[codes].reshape(xb.shape) * np.ldexp(1.0, e_ref)[:, :, None]
+    ya = np.abs(y)
+    step = np.where(ya >= 2.0 ** -6, np.ldexp(1.0, np.floor(np.log2(np.maximum(ya, 1e-300))).astype(int) - 3),
+                    2.0 ** -9)
+    assert (np.abs(deq - xb) <= 0.5 * step * np.ldexp(1.0, e_ref)[:, :, None] * (1 + 1e-15)).all()
+
+
 ALL_PINS = [pin_e4m3_table, pin_single_key, pin_equal_scores, pin_mpmath_bruteforce,
             pin_sdpa, pin_page_permutation, pin_causal_prefix, pin_split_merge,
-            pin_bounds_and_dominant]
+            pin_bounds_and_dominant, pin_sinks_equal_scores, pin_sinks_logaddexp,
+            pin_sinks_mpmath, pin_bf16_rounding, pin_mxfp8]

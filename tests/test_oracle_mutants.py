@@ -25,6 +25,20 @@ MUTANTS = [
     ("subnormal_exponent", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
     ("v_from_rope", "acc[d] += w * J->table[v[d]];", "acc[d] += w * J->table[v[d + 64]];"),
     ("no_max_shift_sign", "double w = exp(s[i] - m);", "double w = exp(m - s[i]);"),
+    ("sink_sign", "double l = J->sinks ? exp(sigma - m) : 0.0;",
+     "double l = J->sinks ? exp(m - sigma) : 0.0;"),
+    ("sink_head_index", "J->sinks[r % J->heads]", "J->sinks[0]"),
+    ("sink_outside_max", "if (sigma > m) m = sigma;", ""),
+    ("bf16_ties_away", "double r = nearbyint(v / quantum) * quantum;",
+     "double r = round(v / quantum) * quantum;"),
+    ("bf16_short_significand", "double quantum = ldexp(1.0, e - 7);",
+     "double quantum = ldexp(1.0, e - 6);"),
+    ("mx_scale_strict", "while (e < 127 && amax > ldexp(448.0, e)) ++e;",
+     "while (e < 127 && amax >= ldexp(448.0, e)) ++e;"),
+    ("mx_ties_odd", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    ("mx_sign_of_zero", "(signbit(y) ? 0x80 : 0)", "(y < 0 ? 0x80 : 0)"),
+    ("mx_amax_skips_first", "for (int i = 0; i < block; ++i) {\n        if (!isfinite",
+     "for (int i = 1; i < block; ++i) {\n        if (!isfinite"),
 ]
 
 
