@@ -13,6 +13,18 @@
 //     out = output_scale * O / l~,   LSE = ln(2) * (M - 8 + log2(l))
 // (the 8 undoes the 2^8 scale of the partials' probabilities). A partial with m = -inf
 // (a split in which a causal row sees no key) contributes nothing.
+//
+// Epilogue options (the steps after the combine in the same PR, and the MXFP8 merge
+// epilogue of TensorRT-LLM PR #17441 "m3 decode perf clean", commit messages):
+//   * sinks: one logit sigma_h per head (units of the scaled scores) joins both sums as
+//     2^(sigma_h log2(e) - M + 8); M is first raised to ceil(sigma_h log2 e) when the
+//     sink is the larger, so the exact power-of-two rescales still apply. LSE is then
+//     the log of the whole denominator.
+//   * MXFP8 O: the BF16 values of O, in blocks of 32 consecutive dims, with an E8M0
+//     scale 2^e, e the smallest integer with amax <= 448 * 2^e (clamped to
+//     [-127, 127]; read off the bits of amax, no division), and E4M3 codes of x / 2^e
+//     (round to nearest even). Four lanes hold one block (8 dims each), so the block
+//     max is two lane swaps.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -37,6 +49,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// E8M0 exponent of an MXFP8 block from its amax (a BF16 value, so exact in fp32): the
+// smallest e with amax <= 448 * 2^e = 1.75 * 2^(e + 8), clamped to [-127, 127].
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = (int)((u >> 23) & 0xFF);
+  if (ef == 0) return -127;  // zero or below 2^-126: the clamp decides
+  const int e = (ef - 127) - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return min(max(e, -127), 127);
+}
+
 struct MergeSmem {
   float o[kMaxGroups][kDV];
   float m[kMaxGroups];
@@ -50,7 +74,7 @@ __global__ void __launch_bounds__(64 * kMaxGroups)
 merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
              const float* __restrict__ oscale_dev, const float* __restrict__ ws_o,
              const float* __restrict__ ws_stats, float output_scale_arg, void* __restrict__ out,
-             float* __restrict__ lse, int groups) {
+             float* __restrict__ lse, int groups, const MergeEpilogue ep) {
   __shared__ MergeSmem sm;
   const PlanDev& P = kDev ? *pdev : Parg;
   const float output_scale = kDev ? *oscale_dev : output_scale_arg;
@@ -109,6 +133,9 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
   float Mx = -INFINITY;
   for (int k = 0; k < G; ++k) Mx = fmaxf(Mx, sm.m[k]);
+  // a sink above every partial's max raises M to its (integer) ceiling
+  const float sig = ep.sinks != nullptr ? ep.sinks[r % P.heads] * kLog2e : -INFINITY;
+  if (sig > Mx) Mx = ceilf(sig);
   float wk[kMaxGroups];
   float L = 0.f, Lt = 0.f;
   for (int k = 0; k < G; ++k) {
@@ -116,15 +143,57 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
     L += wk[k] * sm.l[k];
     Lt += wk[k] * sm.lt[k];
   }
+  if (sig > -INFINITY) {
+    const float ps = exp2f(sig - Mx + 8.f);
+    L += ps;
+    Lt += ps;
+  }
   const float inv = Lt > 0.f ? output_scale / Lt : 0.f;
-  for (int d = threadIdx.x; d < kDV; d += blockDim.x) {
-    float acc = 0.f;
-    for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d];
-    const float v = acc * inv;
-    if (kF32Out)
-      ((float*)out)[(int64_t)row_global * kDV + d] = v;
-    else
-      ((uint16_t*)out)[(int64_t)row_global * kDV + d] = f32_to_bf16_rne(v);
+  if (kF32Out || ep.o_fp8 == nullptr) {
+    for (int d = threadIdx.x; d < kDV; d += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d];
+      const float v = acc * inv;
+      if (kF32Out)
+        ((float*)out)[(int64_t)row_global * kDV + d] = v;
+      else
+        ((uint16_t*)out)[(int64_t)row_global * kDV + d] = f32_to_bf16_rne(v);
+    }
+  } else if (threadIdx.x < 64) {
+    // MXFP8 (and BF16 when out is given): lane t owns dims 8t .. 8t + 7
+    const int d0 = 8 * (int)threadIdx.x;
+    float vb[8];
+    uint32_t hw[4];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float acc = 0.f;
+      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d0 + i];
+      const uint16_t h16 = f32_to_bf16_rne(acc * inv);
+      vb[i] = __uint_as_float((uint32_t)h16 << 16);
+      amax = fmaxf(amax, fabsf(vb[i]));
+      if (i & 1)
+        hw[i >> 1] |= (uint32_t)h16 << 16;
+      else
+        hw[i >> 1] = h16;
+    }
+    if (out != nullptr)
+      *(uint4*)((uint16_t*)out + (int64_t)row_global * kDV + d0) =
+          make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int e = mx_block_exponent(amax);
+    int c0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(vb[0], -e),
+                                             __builtin_amdgcn_ldexpf(vb[1], -e), 0, false);
+    c0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(vb[2], -e),
+                                         __builtin_amdgcn_ldexpf(vb[3], -e), c0, true);
+    int c1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(vb[4], -e),
+                                             __builtin_amdgcn_ldexpf(vb[5], -e), 0, false);
+    c1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(vb[6], -e),
+                                         __builtin_amdgcn_ldexpf(vb[7], -e), c1, true);
+    *(uint2*)(ep.o_fp8 + (int64_t)row_global * kDV + d0) = make_uint2((uint32_t)c0, (uint32_t)c1);
+    if ((threadIdx.x & 3) == 0)
+      ep.o_fp8_scales[(int64_t)row_global * (kDV / 32) + (threadIdx.x >> 2)] = (uint8_t)(e + 127);
   }
   if (lse != nullptr && threadIdx.x == 0)
     lse[row_global] = L > 0.f ? 0.69314718055994531f * ((Mx - 8.f) + log2f(L)) : -INFINITY;
@@ -134,24 +203,25 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
-                 const DeviceArgs* dev) {
+                 const DeviceArgs* dev, const MergeEpilogue* epi) {
   const PlanDev& P = plan.dev;
   const int rows_total = P.batch * P.rows;
   const int groups = plan.merge_groups;
   const PlanDev* pd = dev ? dev->plan : nullptr;
   const float* od = dev ? dev->output_scale : nullptr;
+  const MergeEpilogue ep = epi ? *epi : MergeEpilogue{nullptr, nullptr, nullptr};
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(rows_total), block(64 * groups);
   if (o_is_f32) {
     if (dev)
-      hipLaunchKernelGGL((merge_kernel<true, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+      hipLaunchKernelGGL((merge_kernel<true, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
     else
-      hipLaunchKernelGGL((merge_kernel<true, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+      hipLaunchKernelGGL((merge_kernel<true, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
   } else {
     if (dev)
-      hipLaunchKernelGGL((merge_kernel<false, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+      hipLaunchKernelGGL((merge_kernel<false, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
     else
-      hipLaunchKernelGGL((merge_kernel<false, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups);
+      hipLaunchKernelGGL((merge_kernel<false, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
   }
   return (int)hipGetLastError();
 }

@@ -97,9 +97,17 @@ int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const u
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
                         const DeviceArgs* dev, const int32_t* q_lens);
+// Optional steps of the merge epilogue (any pointer may be null): per-head sink logits
+// (fp32 [H]), and the MXFP8 form of O (E4M3 codes [rows][512], E8M0 scales [rows][16];
+// both or neither). With o_fp8 set, o (BF16) may be null.
+struct MergeEpilogue {
+  const float* sinks;
+  uint8_t* o_fp8;
+  uint8_t* o_fp8_scales;
+};
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
-                 const DeviceArgs* dev = nullptr);
+                 const DeviceArgs* dev = nullptr, const MergeEpilogue* epi = nullptr);
 int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,
                        void* stream);
 

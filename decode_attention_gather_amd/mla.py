@@ -30,7 +30,8 @@ EXPORTS = [
     "mla_decode_plan", "mla_decode_plan_graph", "mla_decode_plan_destroy",
     "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_partial",
     "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
-    "mla_decode_graph", "mla_decode_strerror",
+    "mla_decode_graph", "mla_decode_merge_ex", "mla_decode_ex", "mla_decode_graph_ex",
+    "mla_decode_strerror",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -74,6 +75,14 @@ _lib.mla_decode_merge_f32.restype = ctypes.c_int
 _lib.mla_decode_merge_f32.argtypes = [_p, _p, _sz, _f32, _p, _p, _p]
 _lib.mla_decode.restype = ctypes.c_int
 _lib.mla_decode.argtypes = [_p, _p, _p, _p, _i64, _p, _f32, _f32, _p, _sz, _p, _p, _p]
+_lib.mla_decode_merge_ex.restype = ctypes.c_int
+_lib.mla_decode_merge_ex.argtypes = [_p, _p, _sz, _f32, _p, _p, _p, _p, _p, _p]
+_lib.mla_decode_ex.restype = ctypes.c_int
+_lib.mla_decode_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _f32, _f32, _p, _p, _sz, _p, _p,
+                               _p, _p, _p]
+_lib.mla_decode_graph_ex.restype = ctypes.c_int
+_lib.mla_decode_graph_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p, _p,
+                                     _p, _p, _p]
 _lib.mla_decode_strerror.restype = ctypes.c_char_p
 _lib.mla_decode_strerror.argtypes = [ctypes.c_int]
 
@@ -215,6 +224,53 @@ def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, o
                                  _ptr(softmax_scale),
                                  _ptr(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
                                  _ptr(lse), _stream(stream)), "mla_decode_graph")
+
+
+def _epilogue_args(o, sinks, o_fp8, o_fp8_scales):
+    if o is not None and o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_cuda):
+        raise TypeError("sinks must be a float32 device tensor [H]")
+    for name, t in (("o_fp8", o_fp8), ("o_fp8_scales", o_fp8_scales)):
+        if t is not None and t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be uint8")
+
+
+def merge_ex(plan: Plan, workspace, output_scale: float, o=None, lse=None, sinks=None,
+             o_fp8=None, o_fp8_scales=None, stream=None):
+    """Merge with the epilogue options: per-head sinks, and the MXFP8 form of O
+    (o_fp8 uint8 [rows, 512] E4M3 codes, o_fp8_scales uint8 [rows, 16] E8M0)."""
+    _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
+    _check(_lib.mla_decode_merge_ex(plan.handle, _ptr(workspace), workspace.numel(),
+                                    float(output_scale), _ptr(sinks), _ptr(o), _ptr(lse),
+                                    _ptr(o_fp8), _ptr(o_fp8_scales), _stream(stream)),
+           "mla_decode_merge_ex")
+
+
+def decode_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
+              output_scale: float, workspace, o=None, lse=None, q_lens=None, sinks=None,
+              o_fp8=None, o_fp8_scales=None, stream=None):
+    _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
+    _check(_lib.mla_decode_ex(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                              block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                              float(softmax_scale), float(output_scale), _ptr(sinks),
+                              _ptr(workspace), workspace.numel(), _ptr(o), _ptr(lse),
+                              _ptr(o_fp8), _ptr(o_fp8_scales), _stream(stream)), "mla_decode_ex")
+
+
+def decode_graph_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, output_scale,
+                    workspace, o=None, lse=None, q_lens=None, sinks=None, o_fp8=None,
+                    o_fp8_scales=None, stream=None):
+    _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
+    for name, t in (("softmax_scale", softmax_scale), ("output_scale", output_scale)):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 device tensor")
+    _check(_lib.mla_decode_graph_ex(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                    block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                    _ptr(softmax_scale), _ptr(output_scale), _ptr(sinks),
+                                    _ptr(workspace), workspace.numel(), _ptr(o), _ptr(lse),
+                                    _ptr(o_fp8), _ptr(o_fp8_scales), _stream(stream)),
+           "mla_decode_graph_ex")
 
 
 @dataclass

@@ -202,6 +202,47 @@ int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* k
                      const float* output_scale, void* workspace, size_t workspace_bytes,
                      void* o, float* lse, void* stream);
 
+/*
+ * Merge epilogue options: the steps after the combine in PR #20380 (Description:
+ * sinks are applied after the groups are combined) and the MXFP8 output of the sparse
+ * decode merge in PR #17441 "m3 decode perf clean" (commit messages: the merge emits
+ * E4M3 values with UE8M0 block scales next to its BF16 O, identical to quantizing that
+ * BF16 tensor afterwards). Each option is off when its pointer is NULL.
+ *   sinks         device fp32 [H]: one sink logit per head, in the units of the scaled
+ *                 scores; it joins the softmax denominator only:
+ *                   O = output_scale * sum_i e^(s_i) v_i / (sum_i e^(s_i) + e^(sigma_h)),
+ *                   LSE = ln(sum_i e^(s_i) + e^(sigma_h));
+ *                 a row that sees no key gives O = 0, LSE = sigma_h.
+ *   o_fp8         device uint8 [B][q_len][H][512], 8-byte aligned: E4M3 (OCP "fn")
+ *                 codes of the BF16 O divided by its block scale, nearest even;
+ *   o_fp8_scales  device uint8 [B][q_len][H][16]: one E8M0 scale (biased by 127) per 32
+ *                 consecutive dims; 2^e with e the smallest integer such that the block's
+ *                 largest |BF16 value| <= 448 * 2^e, clamped to [-127, 127].
+ *                 o_fp8 and o_fp8_scales are given together or not at all.
+ *   o             BF16 O as for mla_decode_merge; may be NULL when o_fp8 is given, and
+ *                 must be 16-byte aligned when both are written.
+ * The BF16 O, LSE and every other argument behave as in the call each variant extends.
+ */
+int mla_decode_merge_ex(const mla_decode_plan_t* plan, const void* workspace,
+                        size_t workspace_bytes, float output_scale, const float* sinks, void* o,
+                        float* lse, void* o_fp8, void* o_fp8_scales, void* stream);
+
+/* mla_decode (q_lens NULL) or mla_decode_varq (q_lens given) with the epilogue options. */
+int mla_decode_ex(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                  const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                  const int32_t* q_lens, float softmax_scale, float output_scale,
+                  const float* sinks, void* workspace, size_t workspace_bytes, void* o,
+                  float* lse, void* o_fp8, void* o_fp8_scales, void* stream);
+
+/* mla_decode_graph with the epilogue options (sinks read from device memory at run time,
+ * so they may change between replays of a captured call). */
+int mla_decode_graph_ex(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                        const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                        const int32_t* q_lens, const float* softmax_scale,
+                        const float* output_scale, const float* sinks, void* workspace,
+                        size_t workspace_bytes, void* o, float* lse, void* o_fp8,
+                        void* o_fp8_scales, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_decode_strerror(int status);
 

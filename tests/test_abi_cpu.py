@@ -271,3 +271,45 @@ def test_graph_and_host_plans_not_interchangeable():
                                h.workspace_size(), fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
     assert lib.mla_decode_varq(g.handle, fake, fake, fake, 4, fake, fake, 0.07, 1.0, fake, need,
                                fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_epilogue_validation_before_launch():
+    """The epilogue variants reject bad pointer combinations on the host."""
+    lib = mla.lib_handle()
+    p = plan([100, 50], 1, 12, 2)
+    ws = p.workspace_size()
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10004)  # 4-byte aligned only
+    nul = None
+    merge = lib.mla_decode_merge_ex
+    # codes without scales, and the reverse
+    assert merge(p.handle, fake, ws, 1.0, nul, fake, nul, fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert merge(p.handle, fake, ws, 1.0, nul, fake, nul, nul, fake, nul) == mla.MLA_ERR_INVALID_ARG
+    # neither BF16 O nor MXFP8 O
+    assert merge(p.handle, fake, ws, 1.0, nul, nul, nul, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # MXFP8 codes need 8-byte alignment; BF16 O written next to them needs 16
+    assert merge(p.handle, fake, ws, 1.0, nul, fake, nul, odd, fake, nul) == mla.MLA_ERR_INVALID_ARG
+    assert merge(p.handle, fake, ws, 1.0, nul, odd, nul, fake, fake, nul) == mla.MLA_ERR_INVALID_ARG
+    # misaligned sinks
+    assert merge(p.handle, fake, ws, 1.0, ctypes.c_void_p(0x10002), fake, nul, nul, nul,
+                 nul) == mla.MLA_ERR_INVALID_ARG
+    # short workspace
+    assert merge(p.handle, fake, ws - 1, 1.0, nul, nul, nul, fake, fake, nul) == mla.MLA_ERR_WORKSPACE
+    dec = lib.mla_decode_ex
+    assert dec(p.handle, fake, fake, fake, 4, fake, ctypes.c_void_p(0x10002), 0.07, 1.0, nul,
+               fake, ws, fake, nul, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert dec(p.handle, fake, fake, fake, 4, fake, nul, 0.07, 1.0, nul, fake, ws, fake, nul,
+               fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # plans and entry points do not mix
+    g = gplan(2, 100)
+    gws = g.workspace_size()
+    assert dec(g.handle, fake, fake, fake, 4, fake, nul, 0.07, 1.0, nul, fake, gws, fake, nul,
+               nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert merge(g.handle, fake, gws, 1.0, nul, fake, nul, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    gex = lib.mla_decode_graph_ex
+    assert gex(p.handle, fake, fake, fake, 4, fake, nul, fake, fake, nul, fake, ws, fake, nul,
+               nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert gex(g.handle, fake, fake, fake, 4, fake, nul, fake, fake, nul, fake, gws, fake, nul,
+               fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert gex(g.handle, fake, fake, fake, 4, fake, nul, nul, fake, nul, fake, gws, fake, nul,
+               nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
