@@ -21,6 +21,11 @@ One extra page (the last one) is filled with the E4M3 NaN code 0x7F; unused bloc
 entries point at it, and the slots of each request's last page past its length are set
 to 0x7F too (NaN poisoning: a kernel that reads a byte it should not turns the result
 into NaN instead of silently passing).
+
+BF16 variant (``kv_dtype="bf16"``, the BF16 kernel the same issue compares against): the
+same draws, cast to bfloat16 by torch (round to nearest even) instead of E4M3, stored as
+int16 bit patterns (q [B, q_len, H, 576], cache [num_pages, 32, 576]); the poison is the
+BF16 NaN 0x7FC0.
 """
 from __future__ import annotations
 
@@ -34,6 +39,7 @@ D_QK = 576
 D_V = 512
 PAGE = 32
 E4M3_NAN = 0x7F
+BF16_NAN = 0x7FC0
 SOFTMAX_SCALE = 0.0722
 OUTPUT_SCALE = 1.0
 _CHUNK_PAGES = 2048
@@ -41,9 +47,10 @@ _CHUNK_PAGES = 2048
 
 @dataclasses.dataclass
 class Case:
-    """One decode batch; tensors live on the CPU (uint8 E4M3 codes, int32 indices)."""
-    q: torch.Tensor            # uint8 [B, q_len, H, 576]
-    kv: torch.Tensor           # uint8 [num_pages, 32, 576]
+    """One decode batch; tensors live on the CPU (uint8 E4M3 codes or int16 BF16 bit
+    patterns, int32 indices)."""
+    q: torch.Tensor            # uint8 / int16 [B, q_len, H, 576]
+    kv: torch.Tensor           # uint8 / int16 [num_pages, 32, 576]
     block_table: torch.Tensor  # int32 [B, max_pages]
     kv_lens: torch.Tensor      # int32 [B]
     q_len: int
@@ -52,6 +59,7 @@ class Case:
     output_scale: float = OUTPUT_SCALE
     split_kv: int = 0          # 0: the planner decides; >0 uniform split count
     name: str = ""
+    kv_dtype: str = "e4m3"     # "e4m3" or "bf16" (q has the cache's type)
 
     @property
     def batch(self) -> int:
@@ -67,8 +75,13 @@ class Case:
 
     @property
     def kv_bytes(self) -> int:
-        """Bytes of KV the method must read: every visible token's 576-byte row once."""
-        return int(self.kv_lens.to(torch.int64).sum().item()) * D_QK
+        """Bytes of KV the method must read: every visible token's row once (576 bytes
+        in E4M3, 1152 in BF16)."""
+        return int(self.kv_lens.to(torch.int64).sum().item()) * D_QK * self.elem_bytes
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.kv_dtype == "bf16" else 1
 
 
 def to_e4m3_codes(x: torch.Tensor) -> torch.Tensor:
@@ -76,13 +89,22 @@ def to_e4m3_codes(x: torch.Tensor) -> torch.Tensor:
     return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+def to_bf16_bits(x: torch.Tensor) -> torch.Tensor:
+    """fp32 -> int16 BF16 bit patterns via torch's cast (round to nearest even)."""
+    return x.to(torch.bfloat16).view(torch.int16)
+
+
 def make_case(kv_lens: Sequence[int] | None, *, num_heads: int, q_len: int, seed: int,
               batch: int | None = None, len_range: tuple[int, int] | None = None,
               split_kv: int = 0, softmax_scale: float = SOFTMAX_SCALE,
               output_scale: float = OUTPUT_SCALE, poison: bool = True,
-              name: str = "") -> Case:
+              name: str = "", kv_dtype: str = "e4m3") -> Case:
     """Build a seeded case. Give ``kv_lens`` explicitly, or ``batch`` and ``len_range``
-    (inclusive) to draw them uniformly."""
+    (inclusive) to draw them uniformly. ``kv_dtype``: "e4m3" or "bf16"."""
+    assert kv_dtype in ("e4m3", "bf16")
+    bf16 = kv_dtype == "bf16"
+    cast = to_bf16_bits if bf16 else to_e4m3_codes
+    nan_code = BF16_NAN if bf16 else E4M3_NAN
     g = torch.Generator().manual_seed(int(seed))
     if kv_lens is None:
         assert batch is not None and len_range is not None
@@ -94,7 +116,7 @@ def make_case(kv_lens: Sequence[int] | None, *, num_heads: int, q_len: int, seed
     B = int(lens.numel())
     assert B >= 1 and int(lens.min()) >= q_len >= 1
 
-    q = to_e4m3_codes(torch.randn(B, q_len, num_heads, D_QK, generator=g))
+    q = cast(torch.randn(B, q_len, num_heads, D_QK, generator=g))
 
     npages = [(int(L) + PAGE - 1) // PAGE for L in lens.tolist()]
     used = sum(npages)
@@ -108,19 +130,19 @@ def make_case(kv_lens: Sequence[int] | None, *, num_heads: int, q_len: int, seed
         bt[b, :n] = perm[off:off + n]
         off += n
 
-    kv = torch.empty((num_pages, PAGE, D_QK), dtype=torch.uint8)
+    kv = torch.empty((num_pages, PAGE, D_QK), dtype=torch.int16 if bf16 else torch.uint8)
     for p0 in range(0, used, _CHUNK_PAGES):
         p1 = min(used, p0 + _CHUNK_PAGES)
-        kv[p0:p1] = to_e4m3_codes(torch.randn(p1 - p0, PAGE, D_QK, generator=g))
-    kv[poison_page].fill_(E4M3_NAN)
+        kv[p0:p1] = cast(torch.randn(p1 - p0, PAGE, D_QK, generator=g))
+    kv[poison_page].fill_(nan_code)
     if poison:
         for b, L in enumerate(lens.tolist()):
             tail = L % PAGE
             if tail:
-                kv[int(bt[b, npages[b] - 1]), tail:, :] = E4M3_NAN
+                kv[int(bt[b, npages[b] - 1]), tail:, :] = nan_code
     return Case(q=q, kv=kv, block_table=bt, kv_lens=lens.to(torch.int32), q_len=q_len,
                 num_heads=num_heads, softmax_scale=softmax_scale,
-                output_scale=output_scale, split_kv=split_kv, name=name)
+                output_scale=output_scale, split_kv=split_kv, name=name, kv_dtype=kv_dtype)
 
 
 # The five workloads (seed = 20260 + index), plus the H12 q1 B16 128K shape that the

@@ -60,8 +60,10 @@ def _load(path: str | None = None):
         lib.oracle_mla_decode_rows_ex.restype = ctypes.c_int
         lib.oracle_mla_decode_rows_ex.argtypes = [
             p, p, p, p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-            ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, p, ctypes.c_int64, p, p,
-            ctypes.c_int]
+            ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, ctypes.c_int, p,
+            ctypes.c_int64, p, p, ctypes.c_int]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_round_bf16.restype = None
         lib.oracle_round_bf16.argtypes = [p, ctypes.c_int64, p]
         lib.oracle_mxfp8_quantize.restype = ctypes.c_int
@@ -73,6 +75,11 @@ def _load(path: str | None = None):
 def e4m3_decode(code: int, lib_path: str | None = None) -> float:
     """fp64 value of one OCP E4M3FN code (NaN for 0x7F / 0xFF)."""
     return _load(lib_path).oracle_e4m3_to_double(int(code) & 0xFF)
+
+
+def bf16_decode(code: int, lib_path: str | None = None) -> float:
+    """fp64 value of one BF16 bit pattern."""
+    return _load(lib_path).oracle_bf16_to_double(int(code) & 0xFFFF)
 
 
 def e4m3_table(lib_path: str | None = None) -> np.ndarray:
@@ -94,18 +101,23 @@ def _np(x, dtype):
 
 def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
                softmax_scale: float, output_scale: float = 1.0, rows=None,
-               nthreads: int = 0, lib_path: str | None = None, sinks=None):
+               nthreads: int = 0, lib_path: str | None = None, sinks=None,
+               kv_dtype: str = "e4m3"):
     """Return (O fp64 [nrows, 512], LSE fp64 [nrows]).
 
-    q: uint8 E4M3 codes [B, q_len, H, 576]; kv_cache: uint8 [P, 32, 576];
+    q: uint8 E4M3 codes [B, q_len, H, 576]; kv_cache: uint8 [P, 32, 576]
+    (kv_dtype "bf16": int16 / uint16 BF16 bit patterns of the same shapes);
     block_table: int32 [B, stride]; kv_lens: int32 [B]. ``rows`` lists flat row ids
     r = (b*q_len + j)*H + h (None: every row in order). The scales are used as given
     (pass the fp32-rounded value when the GPU side takes fp32). ``sinks``: per-head
     sink logits [H] (None: no sink), in the units of the scaled scores.
     """
     lib = _load(lib_path)
-    qa = _np(q, np.uint8)
-    kva = _np(kv_cache, np.uint8)
+    assert kv_dtype in ("e4m3", "bf16")
+    bf16 = kv_dtype == "bf16"
+    elem = np.uint16 if bf16 else np.uint8
+    qa = _np(q, elem)
+    kva = _np(kv_cache, elem)
     bta = _np(block_table, np.int32)
     kla = _np(kv_lens, np.int32)
     B = kla.shape[0]
@@ -124,18 +136,21 @@ def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
         rows_ptr = rows_arr.ctypes.data
     o = np.empty((nrows, D_V), dtype=np.float64)
     lse = np.empty((nrows,), dtype=np.float64)
-    if sinks is None:
+    if sinks is None and not bf16:
         rc = lib.oracle_mla_decode_rows(
             qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
             num_heads, stride, num_pages, float(softmax_scale), float(output_scale), rows_ptr,
             nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
     else:
-        sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float64).reshape(-1))
-        assert sk.size == num_heads, "one sink per head"
+        sk = None
+        if sinks is not None:
+            sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float64).reshape(-1))
+            assert sk.size == num_heads, "one sink per head"
         rc = lib.oracle_mla_decode_rows_ex(
             qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
             num_heads, stride, num_pages, float(softmax_scale), float(output_scale),
-            sk.ctypes.data, rows_ptr, nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
+            None if sk is None else sk.ctypes.data, int(bf16), rows_ptr, nrows,
+            o.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_mla_decode_rows failed with code {rc}")
     return o, lse

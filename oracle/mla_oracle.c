@@ -36,6 +36,14 @@
  * there is no infinity. Every E4M3 value is exact in fp64 (and in BF16, as PR #17441
  * "m3 decode perf clean" notes for the widening of E4M3 to BF16).
  *
+ * BF16 cache variant [issue #20510, Repro 2: the BF16 kernel measured beside the FP8
+ * one]: q and the cache hold BF16 values instead (1 sign bit, 8 exponent bits with bias
+ * 127, 7 mantissa bits, subnormals m * 2^-133, exponent 255 for infinities and NaN);
+ * rows are 576 BF16 values (1152 bytes) and everything else is unchanged. BF16 values
+ * are exact in fp64; a BF16 dot product is not always exact in fp64 (the product
+ * exponents can span more than 53 bits), so there the sum is the fp64 sum in dimension
+ * order.
+ *
  * Exactness of the dot product: every E4M3 product is a multiple of 2^-18 with
  * magnitude below 2^18, so every partial sum of at most 576 of them is a multiple of
  * 2^-18 below 2^28 and fits fp64's 53-bit significand; the sum is exact in any order.
@@ -89,6 +97,20 @@ double oracle_e4m3_to_double(uint8_t code) {
   return sign ? -v : v;
 }
 
+/* Decode one BF16 bit pattern to fp64. */
+double oracle_bf16_to_double(uint16_t code) {
+  int sign = code >> 15;
+  int expo = (code >> 7) & 0xFF;
+  int mant = code & 0x7F;
+  double v;
+  if (expo == 0xFF) return mant ? NAN : (sign ? -INFINITY : INFINITY);
+  if (expo == 0)
+    v = ldexp((double)mant, -126 - 7);          /* 0.mmmmmmm * 2^-126 */
+  else
+    v = ldexp(128.0 + mant, expo - 127 - 7);    /* 1.mmmmmmm * 2^(e-127) */
+  return sign ? -v : v;
+}
+
 int oracle_hw_threads(void) {
   long n = sysconf(_SC_NPROCESSORS_ONLN);
   return n > 0 ? (int)n : 1;
@@ -103,6 +125,8 @@ typedef struct {
   int64_t bt_stride, num_pages;
   double softmax_scale, output_scale;
   const double* sinks; /* [heads] extra logits, or NULL */
+  int bf16;            /* 0: E4M3 elements (1 byte), 1: BF16 elements (2 bytes) */
+  double* table16;     /* BF16 decode table (65536 entries) when bf16 */
   const int64_t* rows;
   int64_t nrows;
   double* out_o;
@@ -118,6 +142,18 @@ typedef struct {
 #define ORACLE_ERR_ROW (-3)
 #define ORACLE_ERR_NOMEM (-4)
 
+/* Decode the 576 elements of one row (of q or of the cache) to fp64. */
+static void decode_row(const oracle_job* J, const uint8_t* src, double* dst) {
+  if (J->bf16) {
+    for (int d = 0; d < ORACLE_D_QK; ++d) {
+      uint16_t code = (uint16_t)(src[2 * d] | (src[2 * d + 1] << 8)); /* little endian */
+      dst[d] = J->table16[code];
+    }
+  } else {
+    for (int d = 0; d < ORACLE_D_QK; ++d) dst[d] = J->table[src[d]];
+  }
+}
+
 static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
   int64_t r = J->rows ? J->rows[idx] : idx;
   int64_t rows_total = (int64_t)J->batch * J->q_len * J->heads;
@@ -130,18 +166,18 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
   if (n < 1) return ORACLE_ERR_ARG;
   if ((n + ORACLE_PAGE - 1) / ORACLE_PAGE > J->bt_stride) return ORACLE_ERR_ARG;
 
-  double qd[ORACLE_D_QK];
-  const uint8_t* qrow = J->q + r * ORACLE_D_QK;
-  for (int d = 0; d < ORACLE_D_QK; ++d) qd[d] = J->table[qrow[d]];
+  const int64_t row_bytes = (int64_t)ORACLE_D_QK * (J->bf16 ? 2 : 1);
+  double qd[ORACLE_D_QK], kd[ORACLE_D_QK];
+  decode_row(J, J->q + r * row_bytes, qd);
 
   /* scores s_i = softmax_scale * (q . K_i) */
   double m = -INFINITY;
   for (int64_t i = 0; i < n; ++i) {
     int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
     if (page < 0 || page >= J->num_pages) return ORACLE_ERR_PAGE;
-    const uint8_t* k = J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;
+    decode_row(J, J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * row_bytes, kd);
     double dot = 0.0;
-    for (int d = 0; d < ORACLE_D_QK; ++d) dot += qd[d] * J->table[k[d]];
+    for (int d = 0; d < ORACLE_D_QK; ++d) dot += qd[d] * kd[d];
     s[i] = J->softmax_scale * dot;
     if (s[i] > m) m = s[i];
   }
@@ -153,10 +189,10 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
   double l = J->sinks ? exp(sigma - m) : 0.0;
   for (int64_t i = 0; i < n; ++i) {
     int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
-    const uint8_t* v = J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;
+    decode_row(J, J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * row_bytes, kd);
     double w = exp(s[i] - m);
     l += w;
-    for (int d = 0; d < ORACLE_D_V; ++d) acc[d] += w * J->table[v[d]];
+    for (int d = 0; d < ORACLE_D_V; ++d) acc[d] += w * kd[d]; /* V: the first 512 */
   }
   double* o = J->out_o + idx * ORACLE_D_V;
   for (int d = 0; d < ORACLE_D_V; ++d) o[d] = J->output_scale * acc[d] / l;
@@ -209,6 +245,7 @@ static void* worker(void* arg) {
  *   bt      int32 [B][bt_stride], page indices into kv
  *   kv_lens int32 [B], each >= q_len
  * sinks   fp64 [H] sink logits (see the header), or NULL for none
+ * bf16    0: q and kv hold E4M3 codes; 1: BF16 bit patterns (2 bytes per element)
  * nthreads <= 0 uses every online core. Returns 0 or a negative error code; on error
  * the outputs are unspecified.
  */
@@ -216,7 +253,7 @@ int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t
                               const int32_t* kv_lens, int32_t batch, int32_t q_len,
                               int32_t num_heads, int64_t bt_stride, int64_t num_pages,
                               double softmax_scale, double output_scale, const double* sinks,
-                              const int64_t* rows, int64_t nrows, double* out_o,
+                              int bf16, const int64_t* rows, int64_t nrows, double* out_o,
                               double* out_lse, int nthreads) {
   if (!q || !kv || !bt || !kv_lens || !out_o || !out_lse) return ORACLE_ERR_ARG;
   if (batch < 1 || q_len < 1 || num_heads < 1 || bt_stride < 1 || num_pages < 1 || nrows < 0)
@@ -235,11 +272,20 @@ int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t
   J->softmax_scale = softmax_scale;
   J->output_scale = output_scale;
   J->sinks = sinks;
+  J->bf16 = bf16 ? 1 : 0;
   J->rows = rows;
   J->nrows = nrows;
   J->out_o = out_o;
   J->out_lse = out_lse;
   for (int c = 0; c < 256; ++c) J->table[c] = oracle_e4m3_to_double((uint8_t)c);
+  if (J->bf16) {
+    J->table16 = (double*)malloc(sizeof(double) * 65536);
+    if (!J->table16) {
+      free(J);
+      return ORACLE_ERR_NOMEM;
+    }
+    for (int c = 0; c < 65536; ++c) J->table16[c] = oracle_bf16_to_double((uint16_t)c);
+  }
 
   int nt = nthreads > 0 ? nthreads : oracle_hw_threads();
   if (nt > nrows) nt = nrows > 0 ? (int)nrows : 1;
@@ -252,6 +298,7 @@ int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t
   worker(J);
   for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
   int rc = J->error;
+  free(J->table16);
   free(J);
   return rc;
 }
@@ -263,8 +310,8 @@ int oracle_mla_decode_rows(const uint8_t* q, const uint8_t* kv, const int32_t* b
                            double softmax_scale, double output_scale, const int64_t* rows,
                            int64_t nrows, double* out_o, double* out_lse, int nthreads) {
   return oracle_mla_decode_rows_ex(q, kv, bt, kv_lens, batch, q_len, num_heads, bt_stride,
-                                   num_pages, softmax_scale, output_scale, NULL, rows, nrows,
-                                   out_o, out_lse, nthreads);
+                                   num_pages, softmax_scale, output_scale, NULL, 0, rows,
+                                   nrows, out_o, out_lse, nthreads);
 }
 
 /*

@@ -35,7 +35,8 @@ def _run(case, lib_path, rows=None, **kw):
                              q_len=case.q_len, num_heads=case.num_heads,
                              softmax_scale=kw.get("softmax_scale", F32_SCALE),
                              output_scale=kw.get("output_scale", case.output_scale),
-                             rows=rows, lib_path=lib_path, sinks=kw.get("sinks"))
+                             rows=rows, lib_path=lib_path, sinks=kw.get("sinks"),
+                             kv_dtype=case.kv_dtype)
 
 
 def _gather(case, b, n):
@@ -47,6 +48,13 @@ def _gather(case, b, n):
 
 def _dec(codes_u8: torch.Tensor) -> torch.Tensor:
     return codes_u8.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _dec_case(case, codes: torch.Tensor) -> torch.Tensor:
+    """fp64 values of q or cache elements of a case, E4M3 or BF16, via torch."""
+    if case.kv_dtype == "bf16":
+        return codes.view(torch.bfloat16).to(torch.float64)
+    return _dec(codes)
 
 
 def pin_e4m3_table(lib_path=None):
@@ -364,7 +372,98 @@ def pin_mxfp8(lib_path=None):
     assert (np.abs(deq - xb) <= 0.5 * step * np.ldexp(1.0, e_ref)[:, :, None] * (1 + 1e-15)).all()
 
 
+# ---- the BF16 cache variant ---------------------------------------------------------
+
+def pin_bf16_table(lib_path=None):
+    """All 65536 BF16 bit patterns against torch's bfloat16 -> float64 conversion."""
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    ours = np.array([oracle.bf16_decode(c, lib_path) for c in range(65536)])
+    nan_o, nan_r = np.isnan(ours), np.isnan(ref)
+    assert (nan_o == nan_r).all() and nan_o.sum() == 2 * 127
+    assert np.array_equal(ours[~nan_o], ref[~nan_r])
+    assert np.array_equal(np.signbit(ours[~nan_o]), np.signbit(ref[~nan_r]))
+
+
+def pin_bf16_sdpa(lib_path=None):
+    """BF16 cache: fp64 torch SDPA (causal for q > 1) and logsumexp on gathered rows."""
+    case = inputs.make_case([3, 40, 97], num_heads=3, q_len=3, seed=51, kv_dtype="bf16",
+                            output_scale=0.5)
+    o, lse = _run(case, lib_path)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        kfull = _dec_case(case, _gather(case, b, L))
+        qb = _dec_case(case, case.q[b]).permute(1, 0, 2).contiguous()
+        k = kfull.unsqueeze(0).expand(case.num_heads, L, inputs.D_QK).contiguous()
+        v = kfull[:, :inputs.D_V].unsqueeze(0).expand(case.num_heads, L, inputs.D_V).contiguous()
+        mask = torch.arange(L).unsqueeze(0) <= (L - case.q_len + torch.arange(case.q_len).unsqueeze(1))
+        out = 0.5 * torch.nn.functional.scaled_dot_product_attention(
+            qb, k, v, attn_mask=mask, scale=F32_SCALE)
+        scores = ((qb @ k.transpose(1, 2)) * F32_SCALE).masked_fill(~mask, float("-inf"))
+        ref_lse = torch.logsumexp(scores, dim=-1)
+        for j in range(case.q_len):
+            for h in range(case.num_heads):
+                r = (b * case.q_len + j) * case.num_heads + h
+                np.testing.assert_allclose(o[r], out[h, j].numpy(), rtol=1e-12, atol=1e-12)
+                assert abs(lse[r] - float(ref_lse[h, j])) <= 1e-12 * max(1.0, abs(lse[r]))
+
+
+def pin_bf16_closed_forms(lib_path=None):
+    """BF16 cache: one key gives O = V_0 exactly and LSE = s_0 (exact rational score,
+    to fp64 rounding); q = 0 gives the mean of the visible V rows and LSE = ln n."""
+    case = inputs.make_case([1, 1], num_heads=2, q_len=1, seed=52, kv_dtype="bf16")
+    o, lse = _run(case, lib_path)
+    for b in range(2):
+        k = _gather(case, b, 1)[0]
+        kv_f = [Fraction(x) for x in _dec_case(case, k).tolist()]
+        for h in range(2):
+            r = b * 2 + h
+            qv = [Fraction(x) for x in _dec_case(case, case.q[b, 0, h]).tolist()]
+            s0 = float(Fraction(F32_SCALE) * sum(a * c for a, c in zip(qv, kv_f)))
+            assert abs(lse[r] - s0) <= 1e-15 * max(1.0, abs(s0)), (lse[r], s0)
+            assert np.array_equal(o[r], _dec_case(case, k[:inputs.D_V]).numpy())
+    case = inputs.make_case([37, 64, 5], num_heads=2, q_len=3, seed=53, kv_dtype="bf16")
+    case.q.zero_()
+    o, lse = _run(case, lib_path)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        for j in range(case.q_len):
+            n = L - case.q_len + j + 1
+            mean = _dec_case(case, _gather(case, b, n)[:, :inputs.D_V]).mean(dim=0).numpy()
+            for h in range(2):
+                r = (b * case.q_len + j) * 2 + h
+                np.testing.assert_allclose(o[r], mean, rtol=1e-13, atol=1e-13)
+                assert abs(lse[r] - math.log(n)) <= 1e-14 * max(1.0, math.log(n))
+
+
+def pin_bf16_mpmath(lib_path=None):
+    """BF16 cache, tiny inputs, against 50-digit arithmetic with no max subtraction."""
+    import mpmath
+    mpmath.mp.dps = 50
+    case = inputs.make_case([4, 9], num_heads=2, q_len=2, seed=54, kv_dtype="bf16")
+    o, lse = _run(case, lib_path)
+    sc = mpmath.mpf(F32_SCALE)
+    for b in range(case.batch):
+        L = int(case.kv_lens[b])
+        for j in range(case.q_len):
+            n = L - case.q_len + j + 1
+            rows = _dec_case(case, _gather(case, b, n)).tolist()
+            for h in range(2):
+                r = (b * case.q_len + j) * 2 + h
+                qv = _dec_case(case, case.q[b, j, h]).tolist()
+                es = [mpmath.exp(sc * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c)
+                                                   for a, c in zip(qv, rows[i])))
+                      for i in range(n)]
+                tot = mpmath.fsum(es)
+                ref_lse = float(mpmath.log(tot))
+                assert abs(lse[r] - ref_lse) <= 1e-13 * max(1.0, abs(ref_lse))
+                for d in range(0, inputs.D_V, 13):
+                    ref = float(mpmath.fsum(es[i] * rows[i][d] for i in range(n)) / tot)
+                    assert abs(o[r, d] - ref) <= 1e-13 * max(1.0, abs(ref)), (d, o[r, d], ref)
+
+
 ALL_PINS = [pin_e4m3_table, pin_single_key, pin_equal_scores, pin_mpmath_bruteforce,
             pin_sdpa, pin_page_permutation, pin_causal_prefix, pin_split_merge,
             pin_bounds_and_dominant, pin_sinks_equal_scores, pin_sinks_logaddexp,
-            pin_sinks_mpmath, pin_bf16_rounding, pin_mxfp8]
+            pin_sinks_mpmath, pin_bf16_rounding, pin_mxfp8, pin_bf16_table, pin_bf16_sdpa,
+            pin_bf16_closed_forms, pin_bf16_mpmath]

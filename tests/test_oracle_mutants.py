@@ -17,13 +17,13 @@ MUTANTS = [
     ("causal_off_by_one", "int64_t n = L - J->q_len + j + 1;", "int64_t n = L - J->q_len + j;"),
     ("drop_rope", "for (int d = 0; d < ORACLE_D_QK; ++d) dot +=",
      "for (int d = 0; d < ORACLE_D_V; ++d) dot +="),
-    ("wrong_slot", "(page * ORACLE_PAGE + i % ORACLE_PAGE) * ORACLE_D_QK;\n    double dot",
-     "(page * ORACLE_PAGE + (i + 1) % ORACLE_PAGE) * ORACLE_D_QK;\n    double dot"),
+    ("wrong_slot", "(page * ORACLE_PAGE + i % ORACLE_PAGE) * row_bytes, kd);\n    double dot",
+     "(page * ORACLE_PAGE + (i + 1) % ORACLE_PAGE) * row_bytes, kd);\n    double dot"),
     ("log2_lse", "J->out_lse[idx] = m + log(l);", "J->out_lse[idx] = m + log2(l);"),
     ("scale_on_lse", "J->out_lse[idx] = m + log(l);",
      "J->out_lse[idx] = m + log(l) + log(J->output_scale);"),
     ("subnormal_exponent", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
-    ("v_from_rope", "acc[d] += w * J->table[v[d]];", "acc[d] += w * J->table[v[d + 64]];"),
+    ("v_from_rope", "acc[d] += w * kd[d];", "acc[d] += w * kd[d + 64];"),
     ("no_max_shift_sign", "double w = exp(s[i] - m);", "double w = exp(m - s[i]);"),
     ("sink_sign", "double l = J->sinks ? exp(sigma - m) : 0.0;",
      "double l = J->sinks ? exp(m - sigma) : 0.0;"),
@@ -37,6 +37,12 @@ MUTANTS = [
      "while (e < 127 && amax >= ldexp(448.0, e)) ++e;"),
     ("mx_ties_odd", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
     ("mx_sign_of_zero", "(signbit(y) ? 0x80 : 0)", "(y < 0 ? 0x80 : 0)"),
+    ("bf16_bias", "v = ldexp(128.0 + mant, expo - 127 - 7);",
+     "v = ldexp(128.0 + mant, expo - 126 - 7);"),
+    ("bf16_row_stride", "(J->bf16 ? 2 : 1)", "(J->bf16 ? 1 : 1)"),
+    ("bf16_byte_order", "(uint16_t)(src[2 * d] | (src[2 * d + 1] << 8))",
+     "(uint16_t)(src[2 * d + 1] | (src[2 * d] << 8))"),
+    ("bf16_subnormal", "v = ldexp((double)mant, -126 - 7);", "v = ldexp((double)mant, -126 - 8);"),
     ("mx_amax_skips_first", "for (int i = 0; i < block; ++i) {\n        if (!isfinite",
      "for (int i = 1; i < block; ++i) {\n        if (!isfinite"),
 ]
