@@ -35,6 +35,20 @@ from decode_attention_gather_amd import inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA peak of the MI355X
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense BF16 MFMA peak of the MI355X
+
+
+def mfma_peak(kv_dtype: str) -> float:
+    return BF16_MFMA_PEAK_TFLOPS if kv_dtype == "bf16" else FP8_MFMA_PEAK_TFLOPS
+
+
+def dominant_kernel(kv_dtype: str, rows: int):
+    """(kernel name, source file) of the partial kernel a plan launches."""
+    if kv_dtype == "bf16":
+        return "partial_bf16_kernel", "partial_bf16.hip"
+    if rows > 32:
+        return "partial_wide_kernel", "partial_wide.hip"
+    return "partial_kernel", "partial.hip"
 FLOP_PER_ROW_TOKEN = 2 * (576 + 512)  # QK^T over 576 dims + PV over 512 dims
 METRIC = "µs per MLA decode call + achieved KV-read HBM GB/s (H12 q1 B16 128K)"
 HEADLINE = "m_b16_h12_q1_128k"
@@ -42,12 +56,13 @@ COLD_BYTES = 512 << 20          # written between calls to evict the 256 MB MALL
 
 
 def algorithmic_bytes(case) -> dict:
-    """Bytes the method must move once: every visible token's 576-byte cache row, the
-    query rows, the block-table entries, and the outputs (BF16 O + fp32 LSE)."""
+    """Bytes the method must move once: every visible token's cache row (576 bytes in
+    E4M3, 1152 in BF16), the query rows, the block-table entries, and the outputs (BF16
+    O + fp32 LSE)."""
     rows = case.rows
     pages = int(sum((int(L) + 31) // 32 for L in case.kv_lens.tolist()))
     kv = case.kv_bytes
-    q = rows * 576
+    q = rows * 576 * case.elem_bytes
     bt = pages * 4
     out = rows * (512 * 2 + 4)
     return dict(kv=kv, q=q, bt=bt, out=out, partial_in=kv + q + bt, total=kv + q + bt + out)
@@ -59,13 +74,13 @@ def algorithmic_flops(kv_lens, q_len, num_heads) -> int:
     return tok * num_heads * FLOP_PER_ROW_TOKEN
 
 
-def profiled_traffic(config: str):
+def profiled_traffic(config: str, kernel: str = "partial_kernel", source: str = "partial.hip"):
     """HBM bytes per partial-kernel launch from the committed rocprofv3 counter summary
-    (profiles/partial_kernel_<config>.md), or None when the kernel source changed since
-    the counters were taken."""
+    (profiles/<kernel>_<config>.md), or None when the kernel source changed since the
+    counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"partial_kernel_{config}.md")
-    src = os.path.join(ROOT, "decode_attention_gather_amd", "csrc", "partial.hip")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}.md")
+    src = os.path.join(ROOT, "decode_attention_gather_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -127,7 +142,7 @@ def bench_plan(mla, dc, q, rows, kv_bytes, kv_lens, split_kv, steps, warmup, col
     """Times mla_decode calls and partial-only launches of one plan."""
     t0 = time.perf_counter()
     plan = mla.Plan(kv_lens, q_len=q.shape[1], num_heads=q.shape[2], split_kv=split_kv,
-                    max_split_kv=128)
+                    max_split_kv=256, kv_dtype=dc.kv_dtype)
     plan_us = (time.perf_counter() - t0) * 1e6
     info, splits, _ = plan.info()
     ws = plan.alloc_workspace()
@@ -162,7 +177,7 @@ def graph_path(mla, dc, q, rows, kv_bytes, steps, warmup):
     and scales) with the plan's length bound at the batch's longest request."""
     lens = dc.kv_lens_host
     plan = mla.Plan.graph(len(lens), q_len=q.shape[1], num_heads=q.shape[2],
-                          max_kv_len=max(lens))
+                          max_kv_len=max(lens), kv_dtype=dc.kv_dtype)
     ws = plan.alloc_workspace()
     o = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
@@ -190,7 +205,8 @@ def q8_sibling(case, q_len=8, seed=20263):
 def graph_timing(mla, dc, case, calls=100, reps=5):
     """Launch-bound check: `calls` mla_decode calls captured in one HIP graph, replayed,
     against a graph of 2 * `calls` one-element kernels (the launch floor)."""
-    plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads, split_kv=0)
+    plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads, split_kv=0,
+                    kv_dtype=dc.kv_dtype)
     ws = plan.alloc_workspace()
     o = torch.empty((case.rows, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((case.rows,), dtype=torch.float32, device="cuda")
@@ -245,7 +261,8 @@ def cpu_baseline(case, budget_rows=None):
     t0 = time.perf_counter()
     oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=case.q_len,
                       num_heads=case.num_heads, softmax_scale=float(np.float32(case.softmax_scale)),
-                      output_scale=case.output_scale, rows=rows, nthreads=threads)
+                      output_scale=case.output_scale, rows=rows, nthreads=threads,
+                      kv_dtype=case.kv_dtype)
     dt = time.perf_counter() - t0
     call_s = dt * case.rows / len(rows)
     return dict(value=round(case.kv_bytes / call_s / 1e9, 4), unit="GB/s", cores=threads,
@@ -265,7 +282,7 @@ def bench_other(mla, name, steps, warmup):
         r = bench_plan(mla, dc, dc.q, c.rows, by["kv"], dc.kv_lens_host, sk, steps, warmup,
                        cold_calls=10)
         r["config"] = name
-        r["mfma_util"] = round(flops / (r["us_per_call"] * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)
+        r["mfma_util"] = round(flops / (r["us_per_call"] * 1e-6) / 1e12 / mfma_peak(c.kv_dtype), 4)
         out.append(r)
     if name.startswith("c1_"):
         out[-1]["graph"] = graph_timing(mla, dc, c)
@@ -353,6 +370,7 @@ def main():
     cpu = None if args.no_cpu else cpu_baseline(case)
 
     achieved = by["partial_in"] / (native["partial_us"] * 1e-6) / 1e9
+    kname, ksrc = dominant_kernel(case.kv_dtype, case.q_len * case.num_heads)
     res = {
         "metric": METRIC,
         "value": native["kv_gbs"],
@@ -365,11 +383,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 in (fp32 accumulate), bf16 out",
+        "dtype": f"{case.kv_dtype} in (fp32 accumulate), bf16 out",
         "data": "synthetic: N(0,1) cast to E4M3, seeded random block table",
         "config": {"workload": name, "batch": case.batch, "kv_len": int(case.kv_lens.max()),
                    "heads": case.num_heads, "q_len": case.q_len, "page": 32,
-                   "split_plan": "planner (one wave, cap 128)", "splits": native["splits"],
+                   "split_plan": "planner (one XCD-aware wave, cap 256)", "splits": native["splits"],
                    "work_items": native["work_items"], "parallelism": "1 GPU"},
         "call": native["call"],
         "cold_mall": native.get("cold_mall"),
@@ -380,9 +398,10 @@ def main():
                                   "work_items")},
         "graph_path": gpath,
         "q8": q8,
-        "roofline": {"bound": "hbm", "kernel": "partial_kernel",
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(name),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(name, kname, ksrc),
                      "bytes_per_launch": by["partial_in"], "us_per_launch": native["partial_us"]},
         "cpu_baseline": None if cpu is None else {k: cpu[k] for k in
                                                   ("value", "unit", "cores", "kind", "sample",

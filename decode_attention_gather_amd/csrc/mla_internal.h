@@ -24,6 +24,7 @@ constexpr int kWideMaxTiles = 6;           // wide kernel: 4 or 6 row tiles (96 
 constexpr int kMaxBatch = MLA_MAX_BATCH;
 constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
+constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroup i runs on XCD i mod 8
 
 // Everything the kernels need from a plan, passed by value as a kernel argument
 // (3.6 KB, under the 4 KB kernel-argument limit). Requests are issued longest split
@@ -61,6 +62,7 @@ __host__ __device__ inline int chunk_pages_of(const PlanDev& P, int b) {
 struct mla_decode_plan_s {
   mla::PlanDev dev;
   int32_t device_lengths;
+  int32_t kv_dtype;       // MLA_KV_E4M3 or MLA_KV_BF16
   int32_t max_kv_len;     // graph plans: upper bound of every device length
   int32_t split_kv;       // graph plans: the uniform bound, 0 = proportional planner
   int32_t max_split_kv;   // graph plans: per-request split cap
@@ -93,6 +95,11 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
                    const DeviceArgs* dev = nullptr, const int32_t* q_lens = nullptr);
+// BF16 cache (rows of 576 BF16 values), blocks of 1 or 2 row tiles.
+int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                        const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                        float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                        const DeviceArgs* dev, const int32_t* q_lens);
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
@@ -108,6 +115,8 @@ struct MergeEpilogue {
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
                  const DeviceArgs* dev = nullptr, const MergeEpilogue* epi = nullptr);
+// Splits that fill the chip once for row blocks of `tiles` (XCD-aware; plan.cpp).
+int64_t split_budget(int32_t num_cus, int32_t tiles);
 int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,
                        void* stream);
 

@@ -2,7 +2,7 @@
 //
 // Prior art: the per-request split plan of TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA
 // decode slower after #19338" (Repro 2: block_split_kvs from the planner, a per-request
-// cap raised to 128 "so that one request can fill the GPU"; follow-up comment: the plan
+// cap raised to 128 so that a single request can occupy the whole GPU; follow-up comment: the plan
 // clamped to [1, split_kv], and a minimum split length of one tile rather than four at
 // short KV) and the grid rule of its Repro 1 (uniform split_kv so that B * split_kv is
 // about one wave). Here a wave is one workgroup per CU on a 256-CU MI355X, and a work
@@ -26,6 +26,20 @@ namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+}  // namespace
+
+// Splits that fill the chip once. Workgroup i runs on XCD i mod 8 and the row blocks of
+// one split are issued to one XCD, so a wave holds floor(CUs per XCD / row blocks)
+// splits per XCD; a plan above that leaves some XCD with more workgroups than CUs and
+// the whole launch waits for a second round there.
+int64_t split_budget(int32_t num_cus, int32_t tiles) {
+  const int64_t per_xcd = (int64_t)(num_cus / kXcds) / tiles;
+  if (per_xcd >= 1) return per_xcd * kXcds;
+  return std::max<int64_t>(1, num_cus / tiles);
+}
+
+namespace {
+
 // Splits wanted per request before clamping.
 void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t max_split,
                  int32_t tiles, int32_t num_cus, std::vector<int64_t>& want) {
@@ -35,11 +49,11 @@ void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t ma
     for (size_t b = 0; b < B; ++b) want[b] = std::min<int64_t>(split_kv, max_split);
     return;
   }
-  // Proportional plan: sum_b S_b * tiles ~= num_cus, S_b proportional to the pages of
-  // request b, so every work item streams about the same number of pages.
+  // Proportional plan: sum_b S_b ~= the one-wave split budget, S_b proportional to the
+  // pages of request b, so every work item streams about the same number of pages.
   int64_t total = 0;
   for (int64_t p : pages) total += p;
-  const double items_per_page = (double)num_cus / ((double)tiles * (double)total);
+  const double items_per_page = (double)split_budget(num_cus, tiles) / (double)total;
   for (size_t b = 0; b < B; ++b) {
     int64_t s = (int64_t)(items_per_page * (double)pages[b]);  // floor: at most one wave
     want[b] = std::max<int64_t>(1, std::min<int64_t>(s, max_split));
@@ -48,10 +62,14 @@ void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t ma
 
 // Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow
 // kernel). More rows: blocks of 4 or 6 tiles (wide kernel), as few as 96-row blocks
-// allow, so that one staged page feeds as many rows as the workgroup holds.
-void row_blocks(int32_t rows, int32_t* tiles, int32_t* nt) {
+// allow, so that one staged page feeds as many rows as the workgroup holds. The BF16
+// cache has only the narrow form: blocks of 2 tiles (the last one possibly 1).
+void row_blocks(int32_t rows, int32_t kv_dtype, int32_t* tiles, int32_t* nt) {
   const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
-  if (tiles16 <= kMaxTilesPerBlock) {
+  if (kv_dtype == MLA_KV_BF16) {
+    *nt = std::min<int32_t>(tiles16, kMaxTilesPerBlock);
+    *tiles = (int32_t)ceil_div(tiles16, *nt);
+  } else if (tiles16 <= kMaxTilesPerBlock) {
     *tiles = 1;
     *nt = tiles16;
   } else {
@@ -73,12 +91,12 @@ int32_t merge_groups_for(int64_t max_s, int64_t rows_total, int32_t num_cus) {
 }  // namespace
 
 int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
-               int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+               int32_t split_kv, int32_t max_split_kv, int32_t num_cus, int32_t kv_dtype,
                mla_decode_plan_s** out) {
   if (out == nullptr) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
   if (kv_lens_host == nullptr || batch < 1 || q_len < 1 || num_heads < 1 || split_kv < 0 ||
-      max_split_kv < 1 || num_cus < 0)
+      max_split_kv < 1 || num_cus < 0 || (kv_dtype != MLA_KV_E4M3 && kv_dtype != MLA_KV_BF16))
     return MLA_ERR_INVALID_ARG;
   if (batch > kMaxBatch || max_split_kv > MLA_MAX_SPLIT_KV ||
       (int64_t)q_len * num_heads > MLA_MAX_ROWS_PER_REQUEST)
@@ -92,7 +110,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
 
   const int32_t rows = q_len * num_heads;
   int32_t tiles, nt;
-  row_blocks(rows, &tiles, &nt);
+  row_blocks(rows, kv_dtype, &tiles, &nt);
   std::vector<int64_t> pages(batch), want;
   for (int32_t b = 0; b < batch; ++b) pages[b] = ceil_div(kv_lens_host[b], kPage);
   want_splits(pages, split_kv, max_split_kv, tiles, num_cus, want);
@@ -105,6 +123,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     return MLA_ERR_NOMEM;
   }
   std::memcpy(plan->kv_lens, kv_lens_host, sizeof(int32_t) * batch);
+  plan->kv_dtype = kv_dtype;
 
   PlanDev& d = plan->dev;
   std::memset(&d, 0, sizeof(d));
@@ -160,16 +179,16 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
 // Graph plan: shapes and upper bounds only; the device planner fills in the splits on
 // every call. Capacity (work items the launches are sized for):
 //   uniform split_kv:  B * max(min(split_kv, cap), ceil(max_pages / 65535))
-//   proportional:      min(B * cap, 2 B + num_cus / row_blocks)   (+ B * ceil(max_pages /
+//   proportional:      min(B * cap, 2 B + split budget)   (+ B * ceil(max_pages /
 //                      65535) beyond 2^21 tokens), since sum_b floor(x_b) <= sum_b x_b and
 //                      the clamps to >= 1 add at most one split per request.
 int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_kv_len,
-                     int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
+                     int32_t split_kv, int32_t max_split_kv, int32_t num_cus, int32_t kv_dtype,
                      mla_decode_plan_s** out) {
   if (out == nullptr) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
   if (batch < 1 || q_len < 1 || num_heads < 1 || max_kv_len < 1 || split_kv < 0 ||
-      max_split_kv < 1 || num_cus < 0)
+      max_split_kv < 1 || num_cus < 0 || (kv_dtype != MLA_KV_E4M3 && kv_dtype != MLA_KV_BF16))
     return MLA_ERR_INVALID_ARG;
   if (batch > kMaxBatch || max_split_kv > MLA_MAX_SPLIT_KV ||
       (int64_t)q_len * num_heads > MLA_MAX_ROWS_PER_REQUEST)
@@ -180,7 +199,7 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   }
   const int32_t rows = q_len * num_heads;
   int32_t tiles, nt;
-  row_blocks(rows, &tiles, &nt);
+  row_blocks(rows, kv_dtype, &tiles, &nt);
   const int64_t max_pages = ceil_div(max_kv_len, kPage);
   const int64_t long_split = ceil_div(max_pages, kMaxChunkPages);  // forced splits per request
   int64_t per_req, cap;
@@ -189,7 +208,7 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
     cap = (int64_t)batch * per_req;
   } else {
     per_req = std::max<int64_t>(max_split_kv, long_split);
-    cap = std::min<int64_t>((int64_t)batch * max_split_kv, 2LL * batch + num_cus / tiles);
+    cap = std::min<int64_t>((int64_t)batch * max_split_kv, 2LL * batch + split_budget(num_cus, tiles));
     if (long_split > 1) cap += (int64_t)batch * long_split;
   }
   per_req = std::min<int64_t>(per_req, max_pages);
@@ -208,6 +227,7 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   d.nt = nt;
   d.total_parts = (int32_t)cap;
   plan->device_lengths = 1;
+  plan->kv_dtype = kv_dtype;
   plan->max_kv_len = max_kv_len;
   plan->split_kv = split_kv;
   plan->max_split_kv = max_split_kv;
@@ -231,14 +251,28 @@ int mla_decode_plan_graph(int32_t batch, int32_t q_len, int32_t num_heads, int32
                           int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
                           mla_decode_plan_t** out) {
   return mla::build_graph_plan(batch, q_len, num_heads, max_kv_len, split_kv, max_split_kv,
-                               num_cus, out);
+                               num_cus, MLA_KV_E4M3, out);
+}
+
+int mla_decode_plan_graph_ex(int32_t batch, int32_t q_len, int32_t num_heads,
+                             int32_t max_kv_len, int32_t split_kv, int32_t max_split_kv,
+                             int32_t num_cus, int32_t kv_dtype, mla_decode_plan_t** out) {
+  return mla::build_graph_plan(batch, q_len, num_heads, max_kv_len, split_kv, max_split_kv,
+                               num_cus, kv_dtype, out);
 }
 
 int mla_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
                     int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
                     int32_t num_cus, mla_decode_plan_t** out) {
   return mla::build_plan(kv_lens_host, batch, q_len, num_heads, split_kv, max_split_kv,
-                         num_cus, out);
+                         num_cus, MLA_KV_E4M3, out);
+}
+
+int mla_decode_plan_ex(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
+                       int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
+                       int32_t num_cus, int32_t kv_dtype, mla_decode_plan_t** out) {
+  return mla::build_plan(kv_lens_host, batch, q_len, num_heads, split_kv, max_split_kv,
+                         num_cus, kv_dtype, out);
 }
 
 void mla_decode_plan_destroy(mla_decode_plan_t* plan) {

@@ -10,7 +10,8 @@
 // One workgroup of 256 threads; thread b owns request b:
 //   L_b = clamp(kv_lens[b], 0, max_kv_len), pages_b = ceil(L_b / 32)
 //   wanted splits: the uniform bound min(split_kv, cap), or the one-wave proportional
-//   rule floor(num_cus pages_b / (row_blocks sum pages)) clamped to [1, cap]
+//   rule floor(budget pages_b / sum pages) clamped to [1, cap], budget = the host
+//   planner's XCD-aware split budget
 //   S_b = clamp(wanted, 1, max(pages_b, 1)), at least ceil(pages_b / 65535),
 //   chunk_b = ceil(pages_b / S_b) pages, S_b = ceil(pages_b / chunk_b)  (no empty split)
 // then the requests are ranked longest chunk first (ties by index, the host planner's
@@ -31,6 +32,7 @@ static_assert(kPlanThreads >= kMaxBatch, "one thread per request");
 struct PlanParams {
   int32_t batch, q_len, heads, rows, tiles, nt;
   int32_t max_kv_len, split_kv, max_split_kv, num_cus, cap_parts, max_groups;
+  int32_t budget;  // splits that fill the chip once
 };
 
 __global__ void __launch_bounds__(kPlanThreads)
@@ -61,7 +63,7 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       want = min(pp.split_kv, pp.max_split_kv);
     } else {
       const double per_page = total_pages > 0
-          ? (double)pp.num_cus / ((double)pp.tiles * (double)total_pages) : 0.0;
+          ? (double)pp.budget / (double)total_pages : 0.0;
       want = (int64_t)(per_page * (double)pages);
       want = max((int64_t)1, min(want, (int64_t)pp.max_split_kv));
     }
@@ -128,6 +130,7 @@ int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, Pl
   pp.num_cus = plan.num_cus;
   pp.cap_parts = d.total_parts;
   pp.max_groups = plan.merge_groups;
+  pp.budget = (int32_t)split_budget(plan.num_cus, d.tiles);
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
                      pp, kv_lens, out);
   return (int)hipGetLastError();

@@ -163,6 +163,12 @@ CONFIGS = {
     # matters most here)
     "s_b8_h12_q8_skewed": dict(kv_lens=[1048576] + [4096] * 7, num_heads=12, q_len=8,
                                split_kv=0, seed=20267),
+    # the BF16 cache beside the FP8 one: B1 1M at H12 q8 (the setting of the BF16 figure
+    # the same issue quotes), and the headline H12 q1 B16 128K shape
+    "b_b1_h12_q8_1m_bf16": dict(kv_lens=[1048576], num_heads=12, q_len=8, split_kv=0,
+                                seed=20268, kv_dtype="bf16"),
+    "b_b16_h12_q1_128k_bf16": dict(kv_lens=[131072] * 16, num_heads=12, q_len=1, split_kv=6,
+                                   seed=20269, kv_dtype="bf16"),
 }
 
 

@@ -27,7 +27,8 @@ MLA_ERR_HIP_BASE = -1000
 D_QK, D_V, PAGE = 576, 512, 32
 
 EXPORTS = [
-    "mla_decode_plan", "mla_decode_plan_graph", "mla_decode_plan_destroy",
+    "mla_decode_plan", "mla_decode_plan_ex", "mla_decode_plan_graph",
+    "mla_decode_plan_graph_ex", "mla_decode_plan_destroy",
     "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_partial",
     "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
     "mla_decode_graph", "mla_decode_merge_ex", "mla_decode_ex", "mla_decode_graph_ex",
@@ -55,6 +56,12 @@ class PlanInfo(ctypes.Structure):
 
 _lib.mla_decode_plan.restype = ctypes.c_int
 _lib.mla_decode_plan.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
+_lib.mla_decode_plan_ex.restype = ctypes.c_int
+_lib.mla_decode_plan_ex.argtypes = [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    ctypes.POINTER(_p)]
+_lib.mla_decode_plan_graph_ex.restype = ctypes.c_int
+_lib.mla_decode_plan_graph_ex.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          ctypes.POINTER(_p)]
 _lib.mla_decode_plan_graph.restype = ctypes.c_int
 _lib.mla_decode_plan_graph.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_p)]
 _lib.mla_decode_graph.restype = ctypes.c_int
@@ -116,15 +123,28 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream))
 
 
+MLA_KV_E4M3, MLA_KV_BF16 = 0, 1
+
+
+def _kv_dtype_code(kv_dtype: str) -> int:
+    codes = {"e4m3": MLA_KV_E4M3, "bf16": MLA_KV_BF16}
+    if kv_dtype not in codes:
+        raise ValueError(f"kv_dtype must be one of {sorted(codes)}")
+    return codes[kv_dtype]
+
+
 class Plan:
-    """Owns an mla_decode_plan_t; freed on close() / garbage collection."""
+    """Owns an mla_decode_plan_t; freed on close() / garbage collection. kv_dtype: "e4m3"
+    (q and cache hold E4M3 codes) or "bf16" (BF16 values)."""
 
     def __init__(self, kv_lens: Sequence[int], *, q_len: int, num_heads: int, split_kv: int = 0,
-                 max_split_kv: int = 128, num_cus: int = 0):
+                 max_split_kv: int = 256, num_cus: int = 0, kv_dtype: str = "e4m3"):
         lens = (ctypes.c_int32 * len(kv_lens))(*[int(x) for x in kv_lens])
         h = ctypes.c_void_p()
-        _check(_lib.mla_decode_plan(lens, len(kv_lens), q_len, num_heads, split_kv, max_split_kv,
-                                    num_cus, ctypes.byref(h)), "mla_decode_plan")
+        _check(_lib.mla_decode_plan_ex(lens, len(kv_lens), q_len, num_heads, split_kv,
+                                       max_split_kv, num_cus, _kv_dtype_code(kv_dtype),
+                                       ctypes.byref(h)), "mla_decode_plan_ex")
+        self.kv_dtype = kv_dtype
         self._h = h
         self._destroy = _lib.mla_decode_plan_destroy  # kept: module globals may be gone at exit
         self.batch = len(kv_lens)
@@ -133,14 +153,16 @@ class Plan:
 
     @classmethod
     def graph(cls, batch: int, *, q_len: int, num_heads: int, max_kv_len: int,
-              split_kv: int = 0, max_split_kv: int = 128, num_cus: int = 0) -> "Plan":
+              split_kv: int = 0, max_split_kv: int = 256, num_cus: int = 0,
+              kv_dtype: str = "e4m3") -> "Plan":
         """A graph plan: shapes and bounds only; the splits are planned on the device from
         the device lengths on every decode_graph() call (capturable in a HIP graph)."""
         self = cls.__new__(cls)
         h = ctypes.c_void_p()
-        _check(_lib.mla_decode_plan_graph(batch, q_len, num_heads, max_kv_len, split_kv,
-                                          max_split_kv, num_cus, ctypes.byref(h)),
-               "mla_decode_plan_graph")
+        _check(_lib.mla_decode_plan_graph_ex(batch, q_len, num_heads, max_kv_len, split_kv,
+                                             max_split_kv, num_cus, _kv_dtype_code(kv_dtype),
+                                             ctypes.byref(h)), "mla_decode_plan_graph_ex")
+        self.kv_dtype = kv_dtype
         self._h = h
         self._destroy = _lib.mla_decode_plan_destroy
         self.batch = batch
@@ -176,8 +198,22 @@ class Plan:
         return torch.empty(max(1, self.workspace_size()), dtype=torch.uint8, device=device)
 
 
+def _check_kv(plan: Plan, q, kv_cache):
+    """q and the cache must hold the plan's element type (1 byte E4M3, 2 bytes BF16) in
+    the [.., 576] / [P, 32, 576] layouts: the kernels address them by that size."""
+    es = 2 if getattr(plan, "kv_dtype", "e4m3") == "bf16" else 1
+    for name, t in (("q", q), ("kv_cache", kv_cache)):
+        if t.element_size() != es or t.shape[-1] != D_QK or not t.is_contiguous():
+            raise TypeError(f"{name}: expected contiguous {plan.kv_dtype} elements "
+                            f"({es} byte(s)) with a last dimension of {D_QK}, got "
+                            f"{t.dtype} {tuple(t.shape)}")
+    if kv_cache.dim() != 3 or kv_cache.shape[1] != PAGE:
+        raise TypeError(f"kv_cache: expected [pages, {PAGE}, {D_QK}], got {tuple(kv_cache.shape)}")
+
+
 def partial(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float, workspace,
             stream=None):
+    _check_kv(plan, q, kv_cache)
     _check(_lib.mla_decode_partial(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
                                    block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
                                    _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -195,6 +231,7 @@ def merge(plan: Plan, workspace, output_scale: float, o, lse=None, stream=None):
 def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
            output_scale: float, workspace, o, lse=None, stream=None, q_lens=None):
     """q_lens (device int32 [B], optional): a ragged batch (mla_decode_varq)."""
+    _check_kv(plan, q, kv_cache)
     if o.dtype != torch.bfloat16:
         raise TypeError("o must be bfloat16")
     if q_lens is not None:
@@ -214,6 +251,7 @@ def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, o
                  workspace, o, lse=None, stream=None, q_lens=None):
     """Device-planned decode: kv_lens, softmax_scale and output_scale are device tensors
     (int32 [B], float32 [1], float32 [1]); nothing here reads them on the host."""
+    _check_kv(plan, q, kv_cache)
     if o.dtype != torch.bfloat16:
         raise TypeError("o must be bfloat16")
     for name, t in (("softmax_scale", softmax_scale), ("output_scale", output_scale)):
@@ -250,6 +288,7 @@ def merge_ex(plan: Plan, workspace, output_scale: float, o=None, lse=None, sinks
 def decode_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
               output_scale: float, workspace, o=None, lse=None, q_lens=None, sinks=None,
               o_fp8=None, o_fp8_scales=None, stream=None):
+    _check_kv(plan, q, kv_cache)
     _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
     _check(_lib.mla_decode_ex(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
                               block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
@@ -261,6 +300,7 @@ def decode_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: floa
 def decode_graph_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, output_scale,
                     workspace, o=None, lse=None, q_lens=None, sinks=None, o_fp8=None,
                     o_fp8_scales=None, stream=None):
+    _check_kv(plan, q, kv_cache)
     _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
     for name, t in (("softmax_scale", softmax_scale), ("output_scale", output_scale)):
         if t.dtype != torch.float32 or not t.is_cuda:
@@ -285,6 +325,7 @@ class DeviceCase:
     num_heads: int
     softmax_scale: float
     output_scale: float
+    kv_dtype: str = "e4m3"
 
 
 def to_device(case, device="cuda") -> DeviceCase:
@@ -292,7 +333,8 @@ def to_device(case, device="cuda") -> DeviceCase:
                       block_table=case.block_table.to(device), kv_lens=case.kv_lens.to(device),
                       kv_lens_host=[int(x) for x in case.kv_lens.tolist()], q_len=case.q_len,
                       num_heads=case.num_heads, softmax_scale=case.softmax_scale,
-                      output_scale=case.output_scale)
+                      output_scale=case.output_scale,
+                      kv_dtype=getattr(case, "kv_dtype", "e4m3"))
 
 
 def run_decode(dc: DeviceCase, plan: Plan, workspace=None, f32_out: bool = False):

@@ -76,6 +76,9 @@ extern "C" {
 #define MLA_MAX_ROWS_PER_REQUEST 4096 /* q_len * num_heads */
 #define MLA_MAX_SPLIT_KV 1024         /* cap on splits per request */
 
+#define MLA_KV_E4M3 0 /* q and cache hold OCP E4M3 codes: 576-byte rows */
+#define MLA_KV_BF16 1 /* q and cache hold BF16 values: 1152-byte rows */
+
 typedef struct mla_decode_plan_s mla_decode_plan_t;
 
 /*
@@ -87,8 +90,8 @@ typedef struct mla_decode_plan_s mla_decode_plan_t;
  *                 described in that issue's follow-up comment);
  *   split_kv == 0 planner: splits per request in proportion to L_b so that all
  *                 (split, row block) work items fill num_cus CUs in one wave, capped at
- *                 max_split_kv (the issue raises that cap to 128 "so that one request
- *                 can fill the GPU");
+ *                 max_split_kv (the issue raises that cap to 128 so that a single
+ *                 request can occupy the whole GPU);
  *   max_split_kv  cap on splits per request, 1 .. MLA_MAX_SPLIT_KV (128 recommended);
  *   num_cus       compute units to fill; 0 = query the current HIP device.
  * Every split holds a whole number of pages and none is empty. Splits are issued
@@ -98,6 +101,19 @@ typedef struct mla_decode_plan_s mla_decode_plan_t;
 int mla_decode_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
                     int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
                     int32_t num_cus, mla_decode_plan_t** out);
+
+/*
+ * As mla_decode_plan, for a cache of the given element type (the BF16 kernel that
+ * issue #20510, Repro 2, measures beside the FP8 one): kv_dtype MLA_KV_E4M3 (what
+ * mla_decode_plan builds) or MLA_KV_BF16. With MLA_KV_BF16, q is BF16 [B][q_len][H][576]
+ * (16-byte aligned) and the cache BF16 [P][32][576] (36,864-byte pages); every call that
+ * takes q and kv_cache reads them with that type, the rest (block table, lengths,
+ * workspace, O, LSE, epilogue options) is unchanged. BF16 rows are processed in blocks
+ * of at most 32 query rows.
+ */
+int mla_decode_plan_ex(const int32_t* kv_lens_host, int32_t batch, int32_t q_len,
+                       int32_t num_heads, int32_t split_kv, int32_t max_split_kv,
+                       int32_t num_cus, int32_t kv_dtype, mla_decode_plan_t** out);
 
 void mla_decode_plan_destroy(mla_decode_plan_t* plan);
 
@@ -195,6 +211,11 @@ int mla_decode_varq(const mla_decode_plan_t* plan, const void* q, const void* kv
 int mla_decode_plan_graph(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_kv_len,
                           int32_t split_kv, int32_t max_split_kv, int32_t num_cus,
                           mla_decode_plan_t** out);
+
+/* Graph plan for a cache of the given element type (see mla_decode_plan_ex). */
+int mla_decode_plan_graph_ex(int32_t batch, int32_t q_len, int32_t num_heads,
+                             int32_t max_kv_len, int32_t split_kv, int32_t max_split_kv,
+                             int32_t num_cus, int32_t kv_dtype, mla_decode_plan_t** out);
 
 int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
                      const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,

@@ -313,3 +313,62 @@ def test_epilogue_validation_before_launch():
                fake, nul, nul) == mla.MLA_ERR_INVALID_ARG
     assert gex(g.handle, fake, fake, fake, 4, fake, nul, nul, fake, nul, fake, gws, fake, nul,
                nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("rows_q,heads,exp_tiles,exp_nt", [
+    (1, 12, 1, 1), (2, 16, 1, 2), (8, 12, 3, 2), (3, 12, 2, 2), (8, 96, 24, 2), (1, 5, 1, 1),
+])
+def test_bf16_plans_use_narrow_row_blocks(rows_q, heads, exp_tiles, exp_nt):
+    """BF16 plans process at most 32 query rows per block (blocks of 2 row tiles)."""
+    p = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=256,
+                 kv_dtype="bf16")
+    info = p.info()[0]
+    assert info.row_tiles == exp_tiles
+    assert info.work_items == info.total_splits * exp_tiles
+    g = mla.Plan.graph(2, q_len=rows_q, num_heads=heads, max_kv_len=4096, num_cus=256,
+                       kv_dtype="bf16")
+    assert g.info()[0].row_tiles == exp_tiles
+
+
+def test_kv_dtype_validation():
+    lib = mla.lib_handle()
+    lens = (ctypes.c_int32 * 1)(100)
+    h = ctypes.c_void_p()
+    assert lib.mla_decode_plan_ex(lens, 1, 1, 12, 0, 128, 256, 2, ctypes.byref(h)) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_plan_graph_ex(1, 1, 12, 100, 0, 128, 256, -1, ctypes.byref(h)) == \
+        mla.MLA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        mla.Plan([100], q_len=1, num_heads=12, num_cus=256, kv_dtype="fp16")
+    # the binding refuses tensors of the other element type before any launch
+    p = mla.Plan([100], q_len=1, num_heads=12, num_cus=256, kv_dtype="bf16")
+    q8 = torch.zeros((1, 1, 12, 576), dtype=torch.uint8)
+    kv8 = torch.zeros((5, 32, 576), dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        mla.partial(p, q8, kv8, torch.zeros((1, 4), dtype=torch.int32),
+                    torch.tensor([100], dtype=torch.int32), 0.07, torch.zeros(256, dtype=torch.uint8))
+    pe = mla.Plan([100], q_len=1, num_heads=12, num_cus=256)
+    with pytest.raises(TypeError):
+        mla.partial(pe, q8.to(torch.int16), kv8.to(torch.int16),
+                    torch.zeros((1, 4), dtype=torch.int32), torch.tensor([100], dtype=torch.int32),
+                    0.07, torch.zeros(256, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("lens,q_len,heads,kv_dtype", [
+    ([1 << 20], 8, 12, "bf16"),          # 3 row blocks: 80 splits, not 85
+    ([1 << 20], 1, 12, "e4m3"),          # one row block: the cap (256) fills the chip
+    ([131072] * 16, 8, 12, "bf16"),
+    ([1 << 20] + [4096] * 7, 8, 12, "e4m3"),
+    ([50000, 3000, 7], 4, 16, "bf16"),
+    ([131072] * 8, 8, 96, "e4m3"),       # 8 row blocks of 96 rows
+])
+def test_planner_wave_fits_every_xcd(lens, q_len, heads, kv_dtype):
+    """Workgroup i runs on XCD i mod 8 with the row blocks of a split on one XCD: the
+    planner's one-wave plan must not put more workgroups on an XCD than it has CUs."""
+    p = mla.Plan(lens, q_len=q_len, num_heads=heads, split_kv=0, max_split_kv=256,
+                 num_cus=256, kv_dtype=kv_dtype)
+    info = p.info()[0]
+    per_xcd = -(-info.total_splits // 8) * info.row_tiles
+    assert per_xcd <= 32, (info.total_splits, info.row_tiles)
+    # and it is not far below one wave: at least 7/8 of the CUs get work
+    assert info.work_items >= 0.85 * (32 // info.row_tiles) * 8 * info.row_tiles, info.work_items
