@@ -96,21 +96,32 @@ def profiled_traffic(config: str, kernel: str = "partial_kernel", source: str = 
 
 def time_steps(fn, steps, warmup, stream):
     """`warmup` untimed calls, then exactly `steps` back-to-back calls bracketed by
-    torch.cuda.synchronize(), with a HIP event on `stream` before the first call and
-    after every call. Returns (total µs / steps, per-call µs array, host wall s)."""
+    torch.cuda.synchronize(), timed by one HIP event pair on `stream` (nothing else is
+    enqueued between the calls). Then a second loop of the same calls with an event
+    after every call gives the per-call distribution. Returns (µs per call of the first
+    loop, per-call µs array of the second, host wall s of the first)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = a.elapsed_time(b) * 1e3 / steps
+    n = min(steps, 50)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     ev[0].record(stream)
-    for i in range(steps):
+    for i in range(n):
         fn()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
-    return ev[0].elapsed_time(ev[steps]) * 1e3 / steps, per, wall
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)])
+    return us, per, wall
 
 
 def time_cold(fn, calls, stream):
@@ -297,7 +308,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default=HEADLINE, choices=sorted(inputs.CONFIGS))
     ap.add_argument("--all", action="store_true", help="also time every other workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -305,6 +316,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--planner-only", action="store_true", help="skip the fixed-split plan")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-path timing")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -341,8 +353,10 @@ def main():
     native = bench_plan(mla, dc, dc.q, case.rows, by["kv"], dc.kv_lens_host, 0, steps, warmup,
                         cold_calls=20)
     print(f"[bench] planner plan: {native['us_per_call']} us/call", file=sys.stderr, flush=True)
-    gpath = graph_path(mla, dc, dc.q, case.rows, by["kv"], steps, warmup)
-    print(f"[bench] graph path: {gpath['us_per_call']} us/call", file=sys.stderr, flush=True)
+    gpath = None
+    if not args.no_graph:
+        gpath = graph_path(mla, dc, dc.q, case.rows, by["kv"], steps, warmup)
+        print(f"[bench] graph path: {gpath['us_per_call']} us/call", file=sys.stderr, flush=True)
 
     q8 = None
     if not args.no_q8 and name == HEADLINE:

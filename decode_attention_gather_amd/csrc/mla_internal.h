@@ -24,6 +24,7 @@ constexpr int kWideMaxTiles = 6;           // wide kernel: 4 or 6 row tiles (96 
 constexpr int kMaxBatch = MLA_MAX_BATCH;
 constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
+constexpr int kMergeWavesPerCu = 32;      // merge launch budget: waves resident per CU
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroup i runs on XCD i mod 8
 
 // Everything the kernels need from a plan, passed by value as a kernel argument

@@ -80,11 +80,13 @@ void row_blocks(int32_t rows, int32_t kv_dtype, int32_t* tiles, int32_t* nt) {
 }
 
 // Merge width: wavefront groups per row, a power of two <= min(16, max splits), halved
-// while rows * groups exceeds 8 waves per CU.
+// while the launch (one workgroup of `groups` waves per row) exceeds what the CUs hold
+// at once: two 16-wave workgroups, 32 waves, per CU (the pages' rule halves the width
+// until the launch fits its two-per-SM budget).
 int32_t merge_groups_for(int64_t max_s, int64_t rows_total, int32_t num_cus) {
   int32_t g = 1;
   while (g * 2 <= 16 && g * 2 <= max_s) g *= 2;
-  while (g > 1 && rows_total * g > 8LL * num_cus) g /= 2;
+  while (g > 1 && rows_total * g > (int64_t)kMergeWavesPerCu * num_cus) g /= 2;
   return g;
 }
 

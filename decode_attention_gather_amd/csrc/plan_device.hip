@@ -106,7 +106,8 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       // merge width by the host planner's rule, from the actual largest split count
       int32_t g = 1;
       while (g * 2 <= 16 && g * 2 <= s_max) g *= 2;
-      while (g > 1 && (int64_t)pp.batch * pp.rows * g > 8LL * pp.num_cus) g /= 2;
+      while (g > 1 && (int64_t)pp.batch * pp.rows * g > (int64_t)kMergeWavesPerCu * pp.num_cus)
+        g /= 2;
       out->groups = min(g, pp.max_groups);
     }
   }

@@ -107,7 +107,10 @@ def test_planner_proportional_and_cap():
 def test_merge_groups_rule():
     assert plan([1048576], 1, 12, 100).info()[0].merge_groups == 16
     assert plan([2048], 1, 12, 4).info()[0].merge_groups == 4
-    assert plan([131072] * 16, 8, 12, 6).info()[0].merge_groups == 1  # 1536 rows fill the GPU
+    assert plan([131072] * 16, 8, 12, 6).info()[0].merge_groups == 4  # 1536 rows x 4 <= 32 x 256
+    assert plan([131072] * 64, 8, 12, 6).info()[0].merge_groups == 1  # 6144 rows fill the GPU
+    # the skewed batch: 768 rows, up to 249 splits: 8 groups (768 x 16 > 8192)
+    assert plan([1 << 20] + [4096] * 7, 8, 12, 0, cap=256).info()[0].merge_groups == 8
     assert plan([100], 1, 12, 1).info()[0].merge_groups == 1
 
 
