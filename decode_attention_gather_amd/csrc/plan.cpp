@@ -80,13 +80,22 @@ void row_blocks(int32_t rows, int32_t kv_dtype, int32_t* tiles, int32_t* nt) {
 }
 
 // Merge width: wavefront groups per row, a power of two <= min(16, max splits), halved
-// while the launch (one workgroup of `groups` waves per row) exceeds what the CUs hold
-// at once: two 16-wave workgroups, 32 waves, per CU (the pages' rule halves the width
-// until the launch fits its two-per-SM budget).
-int32_t merge_groups_for(int64_t max_s, int64_t rows_total, int32_t num_cus) {
+// while the waves that fold partials, sum over requests of rows x min(groups, S_b),
+// exceed what the CUs hold at once: two 16-wave workgroups, 32 waves, per CU (the
+// pages' rule halves the width until the launch fits its two-per-SM budget). Groups
+// beyond a row's split count have nothing to fold and end at once, so a short request
+// beside a long one (a skewed batch) does not hold the long one's rows to a narrow merge.
+int32_t merge_groups_for(const std::vector<int64_t>& splits, int64_t rows, int32_t num_cus) {
+  int64_t max_s = 0;
+  for (int64_t sb : splits) max_s = std::max(max_s, sb);
   int32_t g = 1;
   while (g * 2 <= 16 && g * 2 <= max_s) g *= 2;
-  while (g > 1 && rows_total * g > (int64_t)kMergeWavesPerCu * num_cus) g /= 2;
+  auto waves = [&](int32_t gg) {
+    int64_t w = 0;
+    for (int64_t sb : splits) w += rows * std::min<int64_t>(gg, sb);
+    return w;
+  };
+  while (g > 1 && waves(g) > (int64_t)kMergeWavesPerCu * num_cus) g /= 2;
   return g;
 }
 
@@ -137,7 +146,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   d.nt = nt;
 
   int64_t total = 0, max_s = 0;
-  std::vector<int64_t> chunk_of(batch);
+  std::vector<int64_t> chunk_of(batch), split_of(batch);
   for (int32_t b = 0; b < batch; ++b) {
     // whole pages per split, no empty split, split length within uint16 pages
     int64_t s = std::max<int64_t>(1, std::min<int64_t>(want[b], pages[b]));
@@ -148,6 +157,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     d.kv_len[b] = (uint32_t)kv_lens_host[b];
     d.part_base[b] = (uint32_t)total;
     chunk_of[b] = chunk;
+    split_of[b] = s;
     total += s;
     max_s = std::max(max_s, s);
   }
@@ -168,7 +178,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     d.sorted[e] = (run << 8) | (uint32_t)order[e];
   }
 
-  plan->merge_groups = merge_groups_for(max_s, (int64_t)batch * rows, num_cus);
+  plan->merge_groups = merge_groups_for(split_of, rows, num_cus);
   d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)max_s;
   plan->num_cus = num_cus;
@@ -234,8 +244,10 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   plan->split_kv = split_kv;
   plan->max_split_kv = max_split_kv;
   plan->kv_lens = nullptr;
-  plan->merge_groups = merge_groups_for(per_req, (int64_t)batch * rows, num_cus);
-  d.groups = plan->merge_groups;  // launch width; the device planner picks <= this
+  // launch width: the widest merge any lengths can ask for (the device planner applies
+  // the budget to the actual splits and picks <= this)
+  plan->merge_groups = merge_groups_for(std::vector<int64_t>(1, per_req), 0, num_cus);
+  d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)per_req;
   plan->num_cus = num_cus;
   plan->ws_plan_bytes = align256(sizeof(PlanDev));

@@ -43,6 +43,7 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
   __shared__ int32_t s_chunk[kMaxBatch];
   __shared__ int32_t s_order[kMaxBatch];
   __shared__ int32_t s_max;
+  __shared__ long long s_waves[5];  // sum_b rows min(16 >> k, S_b), k = 0..4
   const int b = threadIdx.x;
   const bool live = b < pp.batch;
 
@@ -77,8 +78,15 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
     out->splits[b] = (uint16_t)s;
   }
   if (b == 0) s_max = 0;
+  if (b < 5) s_waves[b] = 0;
   __syncthreads();
-  if (live) atomicMax(&s_max, s_splits[b]);  // LDS atomic
+  if (live) {
+    atomicMax(&s_max, s_splits[b]);  // LDS atomics
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+      atomicAdd((unsigned long long*)&s_waves[k],
+                (unsigned long long)pp.rows * (unsigned long long)min(16 >> k, s_splits[b]));
+  }
   if (live) {
     int32_t base = 0, rank = 0;
     for (int i = 0; i < pp.batch; ++i) {
@@ -103,11 +111,11 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       // construction; the clamp only keeps a broken bound from reading past them)
       out->total_parts = (int32_t)min(run, (uint32_t)pp.cap_parts);
       out->nt = pp.nt;
-      // merge width by the host planner's rule, from the actual largest split count
+      // merge width by the host planner's rule, from the actual splits
       int32_t g = 1;
       while (g * 2 <= 16 && g * 2 <= s_max) g *= 2;
-      while (g > 1 && (int64_t)pp.batch * pp.rows * g > (int64_t)kMergeWavesPerCu * pp.num_cus)
-        g /= 2;
+      auto waves = [&](int32_t gg) { return s_waves[__builtin_ctz(16 / gg)]; };
+      while (g > 1 && waves(g) > (long long)kMergeWavesPerCu * pp.num_cus) g /= 2;
       out->groups = min(g, pp.max_groups);
     }
   }

@@ -109,8 +109,11 @@ def test_merge_groups_rule():
     assert plan([2048], 1, 12, 4).info()[0].merge_groups == 4
     assert plan([131072] * 16, 8, 12, 6).info()[0].merge_groups == 4  # 1536 rows x 4 <= 32 x 256
     assert plan([131072] * 64, 8, 12, 6).info()[0].merge_groups == 1  # 6144 rows fill the GPU
-    # the skewed batch: 768 rows, up to 249 splits: 8 groups (768 x 16 > 8192)
-    assert plan([1 << 20] + [4096] * 7, 8, 12, 0, cap=256).info()[0].merge_groups == 8
+    # the skewed batch: 96 rows of the long request fold 249 partials with 16 groups;
+    # the 672 rows of one-split requests use one group each (2208 waves <= 8192)
+    assert plan([1 << 20] + [4096] * 7, 8, 12, 0, cap=256).info()[0].merge_groups == 16
+    # but 64 requests of 16 splits each at q8 H12: 6144 rows x 16 > 8192 -> 1
+    assert plan([131072] * 64, 8, 12, 16).info()[0].merge_groups == 1
     assert plan([100], 1, 12, 1).info()[0].merge_groups == 1
 
 
