@@ -243,31 +243,36 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
   auto qk_step = [&](int st) {
     const uint8_t* stage = sm.pages[st % kStages];
     float cpg[kT][kStepPages], xs[kT][kStepPages];
+    // K fragments of block (page p, token tile tt): 4 x 32 latent bytes + 2 x 8 rope
+    // bytes per lane. The fragments of the next block are read while this block's MFMAs
+    // run (two buffers), so the LDS latency is paid once per step, not once per block.
+    struct KFrag { v8i kf[4]; long r0, r1; };
+    auto load_frag = [&](int p, int tt, KFrag& f) {
+      const uint8_t* rowp = stage + p * kPageBytes + (16 * tt + l16) * kDQK;
 #pragma unroll
-    for (int p = 0; p < kStepPages; ++p) {
-      v4f sacc[kT][2];
+      for (int c4 = 0; c4 < 4; ++c4)
+        f.kf[c4] = cat8(ld16(rowp, k_off + 128 * c4), ld16(rowp, k_off + 128 * c4 + 16));
+      f.r0 = *(const long*)(rowp + r_off0);
+      f.r1 = *(const long*)(rowp + r_off1);
+    };
+    // QK^T of block (page p, token tile tt) into out[k] for the wave's row tiles
+    auto mfma_block = [&](const KFrag& f, v4f (&out)[kT]) {
+      v4f a4[kT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const uint8_t* rowp = stage + p * kPageBytes + (16 * tt + l16) * kDQK;
-        v4f a4[kT];
+      for (int k = 0; k < kT; ++k) a4[k] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < kT; ++k) a4[k] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const v8i kf = cat8(ld16(rowp, k_off + 128 * c4), ld16(rowp, k_off + 128 * c4 + 16));
+        for (int k = 0; k < kT; ++k)
+          a4[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.kf[c4], qf[k][c4], a4[k], 0, 0, 0, 127, 0, 127);
 #pragma unroll
-          for (int k = 0; k < kT; ++k)
-            a4[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qf[k][c4], a4[k], 0, 0, 0, 127, 0, 127);
-        }
-        const long r0 = *(const long*)(rowp + r_off0);
-        const long r1 = *(const long*)(rowp + r_off1);
-#pragma unroll
-        for (int k = 0; k < kT; ++k) {
-          const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r0, qr[k][0], a4[k], 0, 0, 0);
-          sacc[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(r1, qr[k][1], a, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < kT; ++k) {
+        const v4f a = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(f.r0, qr[k][0], a4[k], 0, 0, 0);
+        out[k] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(f.r1, qr[k][1], a, 0, 0, 0);
       }
+    };
+    // softmax of page p from its two token tiles: P~ to LDS, (c, sum x) kept
+    auto softmax_page = [&](int p, const v4f (&s0)[kT], const v4f (&s1)[kT]) {
       // lane holds S[row l16][page token 16 tt + 4 g + jj]
       const int tok_page = (p_first + st * kStepPages + p) * kPage;
       const bool need_mask = tok_page + kPage > lim_all;
@@ -275,9 +280,10 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
       for (int k = 0; k < kT; ++k) {
         float t[2][4];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) t[tt][jj] = sacc[k][tt][jj] * it.scale_log2;
+        for (int jj = 0; jj < 4; ++jj) {
+          t[0][jj] = s0[k][jj] * it.scale_log2;
+          t[1][jj] = s1[k][jj] * it.scale_log2;
+        }
         if (need_mask) {  // uniform: only pages that reach the split's end or a causal limit
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
@@ -316,7 +322,29 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
         cpg[k][p] = c;
         xs[k][p] = sx;
       }
-    }
+    };
+    // blocks 0 .. 3 = (page 0, tt 0), (0, 1), (1, 0), (1, 1). The K reads of blocks 1
+    // and 2 go out before the previous block's MFMAs; page 0's softmax (VALU) is issued
+    // with block 2's MFMAs so that it runs while the matrix cores work on page 1; block
+    // 3's reads follow it (holding them earlier would not fit the register budget).
+    KFrag fa, fb;
+    v4f s00[kT], s01[kT], s10[kT], s11[kT];
+    load_frag(0, 0, fa);
+    load_frag(0, 1, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(fa, s00);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(1, 0, fa);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(fb, s01);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(fa, s10);
+    softmax_page(0, s00, s01);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(1, 1, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(fb, s11);
+    softmax_page(1, s10, s11);
     // step bookkeeping: new running max, rescale factor, page exponents, l
 #pragma unroll
     for (int k = 0; k < kT; ++k) {
