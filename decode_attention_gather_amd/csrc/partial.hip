@@ -360,11 +360,9 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
       const int valid = t1 - (p_first + st * kStepPages) * kPage;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (16 * g + 4 * q4 + j < valid) m |= 0xFFu << (8 * j);
-        mk[q4] = m;
+        // byte j of word q4 is token 16 g + 4 q4 + j: the first nb bytes are valid
+        const int nb = min(max(valid - (16 * g + 4 * q4), 0), 4);
+        mk[q4] = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
       }
     }
 #pragma unroll

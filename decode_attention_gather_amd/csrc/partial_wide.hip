@@ -491,11 +491,9 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
       const int valid = t1 - (p_first + st * kStepPages) * kPage;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (32 * (g >> 1) + 16 * (wd >> 1) + 8 * (g & 1) + 4 * (wd & 1) + j < valid) m |= 0xFFu << (8 * j);
-        mk[wd] = m;
+        // the first nb bytes of the word are valid
+        const int nb = min(max(valid - (32 * (g >> 1) + 16 * (wd >> 1) + 8 * (g & 1) + 4 * (wd & 1)), 0), 4);
+        mk[wd] = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
       }
     }
 #pragma unroll
