@@ -419,10 +419,13 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     src2[i / 2] = v;
   }
   const bool ld_page_b = (pv * R::kDMA) >= kPageLoads;
-  auto issue = [&](int st) {
+  // block-table index of this wave's page in step st (odd tail: reload page a)
+  auto page_of = [&](int st) {
     const int pa = p_first + st * kStepPages;
-    const int pg = ld_page_b ? min(pa + 1, p_end - 1) : pa;  // odd tail: reload page a
-    const uint64_t gp = uniform_addr(it.kv + (int64_t)it.btb[pg] * kPageBytes);
+    return ld_page_b ? min(pa + 1, p_end - 1) : pa;
+  };
+  auto issue = [&](int st, int64_t id) {
+    const uint64_t gp = uniform_addr(it.kv + id * kPageBytes);
     uint8_t* stage = sm.pages[st % kStages];
 #pragma unroll
     for (int i = 0; i < R::kDMA; ++i) {
@@ -528,15 +531,21 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     }
   };
 
-  // ---- pipeline: 1 + nsteps barriers, like the QK waves
-  if (nsteps > 0) issue(0);
-  if (nsteps > 1) issue(1);
+  // ---- pipeline: 1 + nsteps barriers, like the QK waves. The page id of a step is
+  // read one step before its loads are issued, so the issue never waits on it.
+  int64_t nid = 0;
+  if (nsteps > 0) issue(0, it.btb[page_of(0)]);
+  if (nsteps > 1) issue(1, it.btb[page_of(1)]);
+  if (nsteps > 2) nid = it.btb[page_of(2)];
   if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // step 0 landed
   block_sync_lds();
   for (int st = 0; st < nsteps; ++st) {
     wait_vmcnt<0>();  // step st + 1 landed
     block_sync_lds();
-    if (st + 2 < nsteps) issue(st + 2);
+    if (st + 2 < nsteps) {
+      issue(st + 2, nid);
+      if (st + 3 < nsteps) nid = it.btb[page_of(st + 3)];
+    }
     pv_step(st);
   }
 
