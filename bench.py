@@ -320,9 +320,10 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the decode path has no multi-GPU sharding in this "
-              "build (requests, heads and KV splits would shard across GPUs; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path is not sharded across GPUs "
+              "(requests, heads and KV splits are the axes it would shard along, with one "
+              "exchange of the per-split partials before the merge). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
