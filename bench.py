@@ -45,6 +45,8 @@ def mfma_peak(kv_dtype: str) -> float:
 def dominant_kernel(kv_dtype: str, rows: int):
     """(kernel name, source file) of the partial kernel a plan launches."""
     if kv_dtype == "bf16":
+        if rows > 32:
+            return "partial_bf16_wide_kernel", "partial_bf16_wide.hip"
         return "partial_bf16_kernel", "partial_bf16.hip"
     if rows > 32:
         return "partial_wide_kernel", "partial_wide.hip"
@@ -399,7 +401,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": f"{case.kv_dtype} in (fp32 accumulate), bf16 out",
-        "data": "synthetic: N(0,1) cast to E4M3, seeded random block table",
+        "data": ("synthetic: N(0,1) cast to "
+                 f"{'BF16' if case.kv_dtype == 'bf16' else 'E4M3'}, seeded random block table"),
         "config": {"workload": name, "batch": case.batch, "kv_len": int(case.kv_lens.max()),
                    "heads": case.num_heads, "q_len": case.q_len, "page": 32,
                    "split_plan": "planner (one XCD-aware wave, cap 256)", "splits": native["splits"],

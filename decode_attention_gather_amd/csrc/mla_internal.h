@@ -101,6 +101,11 @@ int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const u
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
                         const DeviceArgs* dev, const int32_t* q_lens);
+// BF16 cache, blocks of 4 or 6 row tiles.
+int launch_partial_bf16_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                             const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                             float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                             const DeviceArgs* dev, const int32_t* q_lens);
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,

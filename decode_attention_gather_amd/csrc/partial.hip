@@ -510,6 +510,9 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
                    const DeviceArgs* dev, const int32_t* q_lens) {
   const PlanDev& P = plan.dev;
+  if (plan.kv_dtype == MLA_KV_BF16 && P.nt > kMaxTilesPerBlock)
+    return launch_partial_bf16_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o,
+                                    ws_stats, stream, dev, q_lens);
   if (plan.kv_dtype == MLA_KV_BF16)
     return launch_partial_bf16(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
                                stream, dev, q_lens);

@@ -62,14 +62,11 @@ void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t ma
 
 // Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow
 // kernel). More rows: blocks of 4 or 6 tiles (wide kernel), as few as 96-row blocks
-// allow, so that one staged page feeds as many rows as the workgroup holds. The BF16
-// cache has only the narrow form: blocks of 2 tiles (the last one possibly 1).
-void row_blocks(int32_t rows, int32_t kv_dtype, int32_t* tiles, int32_t* nt) {
+// allow, so that one staged page feeds as many rows as the workgroup holds. Both cache
+// types follow the rule (each has a narrow and a wide kernel).
+void row_blocks(int32_t rows, int32_t* tiles, int32_t* nt) {
   const int32_t tiles16 = (int32_t)ceil_div(rows, kTileRows);
-  if (kv_dtype == MLA_KV_BF16) {
-    *nt = std::min<int32_t>(tiles16, kMaxTilesPerBlock);
-    *tiles = (int32_t)ceil_div(tiles16, *nt);
-  } else if (tiles16 <= kMaxTilesPerBlock) {
+  if (tiles16 <= kMaxTilesPerBlock) {
     *tiles = 1;
     *nt = tiles16;
   } else {
@@ -121,7 +118,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
 
   const int32_t rows = q_len * num_heads;
   int32_t tiles, nt;
-  row_blocks(rows, kv_dtype, &tiles, &nt);
+  row_blocks(rows, &tiles, &nt);
   std::vector<int64_t> pages(batch), want;
   for (int32_t b = 0; b < batch; ++b) pages[b] = ceil_div(kv_lens_host[b], kPage);
   want_splits(pages, split_kv, max_split_kv, tiles, num_cus, want);
@@ -211,7 +208,7 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   }
   const int32_t rows = q_len * num_heads;
   int32_t tiles, nt;
-  row_blocks(rows, kv_dtype, &tiles, &nt);
+  row_blocks(rows, &tiles, &nt);
   const int64_t max_pages = ceil_div(max_kv_len, kPage);
   const int64_t long_split = ceil_div(max_pages, kMaxChunkPages);  // forced splits per request
   int64_t per_req, cap;

@@ -321,11 +321,12 @@ def test_epilogue_validation_before_launch():
                nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("rows_q,heads,exp_tiles,exp_nt", [
-    (1, 12, 1, 1), (2, 16, 1, 2), (8, 12, 3, 2), (3, 12, 2, 2), (8, 96, 24, 2), (1, 5, 1, 1),
+@pytest.mark.parametrize("rows_q,heads,exp_tiles", [
+    (1, 12, 1), (2, 16, 1), (8, 12, 1), (3, 12, 1), (8, 96, 8), (1, 5, 1), (7, 16, 2),
 ])
-def test_bf16_plans_use_narrow_row_blocks(rows_q, heads, exp_tiles, exp_nt):
-    """BF16 plans process at most 32 query rows per block (blocks of 2 row tiles)."""
+def test_bf16_plans_share_the_row_block_rule(rows_q, heads, exp_tiles):
+    """BF16 plans block rows as E4M3 plans do: up to 32 rows in one block, more in as
+    few blocks of at most 96 rows as cover them."""
     p = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=256,
                  kv_dtype="bf16")
     info = p.info()[0]
@@ -361,7 +362,7 @@ def test_kv_dtype_validation():
 
 
 @pytest.mark.parametrize("lens,q_len,heads,kv_dtype", [
-    ([1 << 20], 8, 12, "bf16"),          # 3 row blocks: 80 splits, not 85
+    ([1 << 20], 8, 12, "bf16"),          # one 96-row block
     ([1 << 20], 1, 12, "e4m3"),          # one row block: the cap (256) fills the chip
     ([131072] * 16, 8, 12, "bf16"),
     ([1 << 20] + [4096] * 7, 8, 12, "e4m3"),

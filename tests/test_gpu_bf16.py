@@ -50,6 +50,11 @@ SMALL = [
     ("q1_single_split_long", [5000], 12, 1, 1),
     ("odd_pages_split2", [3 * 32 + 7, 5 * 32], 12, 1, 2),
     ("q8_last_split_one_token", [65, 97], 12, 8, 3),
+    # wide row blocks: ragged row counts inside a block, two blocks, two-page splits
+    ("q7_h16_two_wide_blocks", [700, 33], 16, 7, 2),
+    ("q13_h5_rows65", [400, 129], 5, 13, 0),
+    ("q5_h16_rows80_split1", [1000], 16, 5, 1),
+    ("q6_h16_two_pages", [64, 40], 16, 6, 1),
 ]
 
 
@@ -73,12 +78,13 @@ def test_bf16_single_key_and_equal_scores(mla):
     assert_parity(o, lse, o_ref, lse_ref, "bf16 special cases")
 
 
-def test_bf16_split_invariance_f32(mla):
-    case = inputs.make_case([3000], num_heads=12, q_len=2, seed=9003, kv_dtype="bf16")
+@pytest.mark.parametrize("q_len", [2, 8])
+def test_bf16_split_invariance_f32(mla, q_len):
+    case = inputs.make_case([3000], num_heads=12, q_len=q_len, seed=9003, kv_dtype="bf16")
     dc = mla.to_device(case)
     outs = []
     for sk in (1, 3, 7, 0):
-        _say(f"[gpu] bf16 split invariance split_kv={sk}")
+        _say(f"[gpu] bf16 split invariance q_len={q_len} split_kv={sk}")
         o, lse, _ = run_bf16(mla, case, split_kv=sk, dc=dc, f32_out=True)
         outs.append((o, lse))
     for o, lse in outs[1:]:
