@@ -3,39 +3,48 @@
 //
 // The BF16 variant that TensorRT-LLM issue #20510 "CuTe DSL FP8 MLA decode slower after
 // #19338" measures beside the FP8 kernel (Repro 2), for requests of more than 32 query
-// rows (q = 8, many heads). It computes exactly what partial_bf16.hip computes, per
-// (request b, split s, block of 16 NT query rows, NT = 4 or 6): the state of PR #20380 "trtllm-gen
-// FMHA: split the KV partials of a row across thread groups in fmhaReductionKernel"
-// (Description: per-row max, sum and unnormalised O) with P~ the BF16 rounding of
-// 2^(t - c + 8) per 16-token tile, scaled by 2^(c - m) before the PV product. Here one
-// staged page feeds up to 96 rows, so a page crosses HBM -> LDS once per 96 rows
-// instead of once per 32.
+// rows (q = 8, many heads). Per (request b, split s, block of 16 NT query rows, NT = 4
+// or 6) it writes the state of PR #20380 "trtllm-gen FMHA: split the KV partials of a
+// row across thread groups in fmhaReductionKernel" (Description: per-row max, sum and
+// unnormalised O) as partial_bf16.hip does: P~ is the BF16 rounding of 2^(t - c + 8)
+// per 16-token tile (c = ceil of the tile's max), times 2^(c - m) with m the running
+// maximum. Here the QK waves form that product before they publish P~: rounding
+// commutes with a power-of-two scale, so the bits are the same wherever P~ is a normal
+// BF16 value (the rest lies more than 2^126 below the row's largest term). One staged
+// page feeds up to 96 rows, so a page crosses HBM -> LDS once per 96 rows instead of
+// once per 32.
 //
 // Design for gfx950: one workgroup of NT/2 + 4 wavefronts per work item (at most 2 per
 // SIMD, so every wave may hold 256 VGPRs).
 //  * Gather: direct-to-LDS loads (global_load_lds_dwordx4, 1 KB per instruction) of one
-//    page (36 KB) per pipeline step into a 3-stage ring, issued by the PV waves two
-//    steps ahead. Rows stay 1152 bytes; 16-byte chunk c of token row n sits at chunk
-//    (c + ((n >> 1) & 7)) mod 72, which puts the 16 rows of an operand read on distinct
-//    LDS banks (a row is 288 dwords, so consecutive rows start half of the 64 banks
-//    apart, and the rotation spreads 8 row pairs over the other half-offsets).
+//    page (36 KB) per pipeline step into a 4-stage ring (160 KB of LDS with P~), issued
+//    by the PV waves three steps ahead between their MFMAs, so a load has two steps to
+//    land. Rows stay 1152 bytes; 16-byte chunk c of token
+//    row n sits at chunk (c + ((n >> 1) & 7)) mod 72, which puts the 16 rows of an
+//    operand read on distinct LDS banks (a row is 288 dwords, so consecutive rows start
+//    half of the 64 banks apart, and the rotation spreads 8 row pairs over the other
+//    offsets). Rows past the split's end are zeroed in LDS once, so V needs no mask.
 //  * QK^T: NT/2 QK waves; wave q holds Q^T of row tiles 2q, 2q + 1 (144 VGPRs: BF16
 //    Q^T of three tiles would not fit beside the accumulators) and forms S^T = K Q^T of
-//    both 16-token tiles of the page on v_mfma_f32_16x16x32_bf16; every K fragment
-//    read feeds two MFMAs. Softmax per (row, tile): c = ceil(max t),
-//    x = 2^(t - c + 8), P~ = BF16(x) to LDS with c; the QK waves also keep each row's
-//    running maximum m and l = sum x, l~ = sum P~ (both scaled to m).
-//  * PV: 4 waves; wave (group pg, half dh) keeps the running maximum m of row tiles
-//    [pg NT/2, (pg + 1) NT/2), scales their P~ rows by 2^(c - m) (exact), and
-//    accumulates O for dims [256 dh, 256 dh + 256) with V gathered transposed by
-//    ds_read_b64_tr_b16; each V read feeds NT/2 MFMAs. With 3 QK waves beside 4 PV
-//    waves (NT = 6) every SIMD but one runs one QK and one PV wave. K position 8 G + 4 tt + j of an MFMA (G = lane group) holds
-//    token 16 tt + 4 G + j, where both the QK results and the transposed reads put it.
+//    both 16-token tiles of the page on v_mfma_f32_16x16x32_bf16, K fragments read two
+//    steps of the dot product ahead; every K fragment feeds two MFMAs. Softmax per row:
+//    c per tile, the new running maximum m, x = 2^(t - c + 8), P~ = BF16(x 2^(c - m))
+//    to LDS with the rescale factor 2^(m_old - m) of the row; l = sum x and l~ = sum P~
+//    (both scaled to m) stay in the QK waves.
+//  * PV: 4 waves; wave (group pg, half dh) accumulates O of row tiles
+//    [pg NT/2, (pg + 1) NT/2) for dims [256 dh, 256 dh + 256), rescaling it when a row's
+//    maximum moved, with V gathered transposed by ds_read_b64_tr_b16 two dim tiles
+//    ahead; each V read feeds NT/2 MFMAs. With 3 QK waves beside 4 PV waves (NT = 6)
+//    every SIMD but one runs one QK and one PV wave. K position 8 G + 4 tt + j of an
+//    MFMA (G = lane group) holds token 16 tt + 4 G + j, where both the QK results and
+//    the transposed reads put it.
 //  * Skewed single-barrier pipeline: iteration s runs QK/softmax of step s + 1 and PV of
-//    step s; P~ and the tile statistics are double-buffered.
+//    step s; P~ and the rescale factors are double-buffered.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "mla_internal.h"
 
@@ -47,15 +56,17 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kRowB = 2 * kDQK;                     // 1152 bytes per token row
 constexpr int kPageB = kPage * kRowB;               // 36864 bytes per page
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kChunks = kRowB / 16;                 // 72 chunks of 16 bytes per row
 constexpr int kLoads = kPageB / 1024;               // 36 wave-wide 16-byte loads per page
 constexpr int kKSteps = kDQK / 32;                  // 18 MFMAs of K = 32 per 576-wide dot
-constexpr int kPRowB = 80;                          // P~ row: 32 BF16 + 16 bytes of pad
+constexpr int kPRowB = 64;                          // P~ row: 32 BF16
 
 // Roles: NT/2 QK waves, wave q holding Q^T of row tiles 2 q, 2 q + 1; 4 PV waves,
 // wave (group pg, half dh) accumulating O of row tiles [pg NT/2, (pg + 1) NT/2) and
@@ -76,14 +87,26 @@ struct BWRoles {
 template <int NT>
 struct __attribute__((aligned(16))) BWSmem {
   uint8_t pages[kStages][kPageB];
-  uint8_t ptile[2][NT * kTileRows * kPRowB];
-  float2 cl[2][NT * kTileRows];  // per row: c of token tiles 0 and 1
+  uint8_t ptile[2][NT * kTileRows * kPRowB];  // P~, scaled to the running maximum
+  float alpha[2][NT * kTileRows];             // per row: 2^(m_old - m_new) of the step
 };
 
 __device__ __forceinline__ int rot_of(int n) { return (n >> 1) & 7; }
 
 __device__ __forceinline__ v4i ld16(const uint8_t* base, int off) {
   return *(const v4i*)(base + off);
+}
+
+// LDS byte address of a shared-memory pointer, and loads from such an address (a
+// constant added to one base register becomes the instruction's offset field).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS uint8_t*)p;
+}
+__device__ __forceinline__ v4i lds_ld16(uint32_t a) {
+  return *(const LDS_AS v4i*)(uintptr_t)a;
+}
+__device__ __forceinline__ v4s lds_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(uintptr_t)a);
 }
 
 __device__ __forceinline__ v8bf as_bf8(v4i x) { return __builtin_bit_cast(v8bf, x); }
@@ -141,13 +164,6 @@ __device__ __forceinline__ float pow2_diff(float a, float b) {
   return a == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(a - b));
 }
 
-// Two BF16 values (one 32-bit word) times a power of two (exact for normal values).
-__device__ __forceinline__ uint32_t scale_bf16x2(uint32_t w, float s) {
-  const float lo = __uint_as_float(w << 16) * s;
-  const float hi = __uint_as_float(w & 0xFFFF0000u) * s;
-  return (__float_as_uint(hi) & 0xFFFF0000u) | (__float_as_uint(lo) >> 16);
-}
-
 __device__ __forceinline__ bool wg_item(const PlanDev& P, int wg, int* part_sorted, int* blk) {
   const int x = wg & 7, k = wg >> 3;
   const int slot = k / P.tiles;
@@ -174,8 +190,7 @@ constexpr int kNoKey = -0x40000000;
 // ------------------------------------------------------------------ QK waves
 template <int NT>
 __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
-  using R = BWRoles<NT>;
-  constexpr int kQKT = R::kQKT, kCh = 2;  // two accumulator chains per row tile
+  constexpr int kQKT = BWRoles<NT>::kQKT;
   const PlanDev& P = *it.P;
   const int g = it.g, l16 = it.l16, qw = it.w;
   const int nsteps = it.nsteps, p_first = it.p_first, t1 = it.t1;
@@ -214,83 +229,126 @@ __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
   // K operand of token row n = 16 tt + l16: chunk 4 kk + g at (4 kk + g + rot(n)) mod 72;
   // rot(n) = (l16 >> 1) & 7 for both tiles. Latent steps (kk < 16) never wrap.
   const int rot = rot_of(l16);
-  const int k_lat = 16 * (g + rot);
-  int k_rope[2];
+  const uint32_t pages0 = lds_addr(sm.pages[0]);
+  const uint32_t k_lat = pages0 + l16 * kRowB + 16 * (g + rot);
+  uint32_t k_rope[2];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) k_rope[r] = 16 * ((64 + 4 * r + g + rot) % kChunks);
+  for (int r = 0; r < 2; ++r)
+    k_rope[r] = pages0 + l16 * kRowB + 16 * ((64 + 4 * r + g + rot) % kChunks);
 
-  auto qk_step = [&](int st) {
-    const uint8_t* stage = sm.pages[st % kStages];
+  int stage_off = 0;  // byte offset of step st's stage; advanced per step
+  const v2bf ones = {(__bf16)1.f, (__bf16)1.f};
+  // One step. Token tile 0's MFMAs run first; the first half of its softmax (scores,
+  // tile maximum c, x = 2^(t - c + 8)) runs between token tile 1's MFMAs. kMasked: the
+  // page holds keys some row may not see (split end, causal limit).
+  auto qk_step = [&](int st, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int tok_page = (p_first + st) * kPage;
-    const bool need_mask = tok_page + kPage > lim_all;
+    v4f acc[kQKT][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint8_t* rowp = stage + (16 * tt + l16) * kRowB;
-      v4f acc[kQKT][kCh];
+    for (int k = 0; k < kQKT; ++k) acc[k][0] = acc[k][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    float t[kQKT][2][4], x[kQKT][2][4], c[kQKT][2], xsum[kQKT][2];
+    // K fragments of token row 16 tt + l16, two steps of the dot product ahead
+    v4i kf[3];
+    auto kload = [&](int tt, int kk, v4i& f) {
+      f = lds_ld16((kk < 16 ? k_lat + 64 * kk : k_rope[kk - 16]) + stage_off + 16 * tt * kRowB);
+    };
+    auto mfma_kk = [&](int tt, int kk) {
 #pragma unroll
       for (int k = 0; k < kQKT; ++k)
-#pragma unroll
-        for (int c = 0; c < kCh; ++c) acc[k][c] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        const int off = kk < 16 ? k_lat + 64 * kk : k_rope[kk - 16];
-        const v8bf kf = as_bf8(ld16(rowp, off));
-#pragma unroll
-        for (int k = 0; k < kQKT; ++k)
-          acc[k][kk % kCh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, as_bf8(qf[k][kk]), acc[k][kk % kCh], 0, 0, 0);
-      }
-      // lane holds S[row l16][page token 16 tt + 4 g + jj]
-      const int tok0 = tok_page + 16 * tt + 4 * g;
-#pragma unroll
-      for (int k = 0; k < kQKT; ++k) {
-        float t[4];
-        float mx = -INFINITY;
+        acc[k][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf8(kf[kk % 3]), as_bf8(qf[k][kk]), acc[k][tt], 0, 0, 0);
+    };
+    // softmax, first half, of (tile k, token tile tt) in four slices
+    auto part1 = [&](int k, int tt, int slice) {
+      if (slice == 0) {
+        const int tok0 = tok_page + 16 * tt + 4 * g;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          float v = (acc[k][0][jj] + acc[k][1][jj]) * it.scale_log2;
-          if (need_mask && tok0 + jj >= lim_q[k]) v = -INFINITY;
-          t[jj] = v;
-          mx = fmaxf(mx, v);
+          float v = acc[k][tt][jj] * it.scale_log2;
+          if (kMasked && tok0 + jj >= lim_q[k]) v = -INFINITY;
+          t[k][tt][jj] = v;
         }
-        mx = group_max4(mx);
-        const float c = ceilf(mx);  // -inf when no key of the tile is visible to the row
-        const float off = 8.f - (c == -INFINITY ? 0.f : c);
-        float xs = 0.f, ps = 0.f;
-        uint32_t pw[2];
+        c[k][tt] = fmaxf(fmaxf(t[k][tt][0], t[k][tt][1]), fmaxf(t[k][tt][2], t[k][tt][3]));
+      } else if (slice == 1) {
+        c[k][tt] = ceilf(group_max4(c[k][tt]));  // -inf when no key of the tile is visible
+      } else if (slice == 2) {
+        const float off = 8.f - (c[k][tt] == -INFINITY ? 0.f : c[k][tt]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float x0 = __builtin_amdgcn_exp2f(t[2 * h] + off);  // exp2(-inf) = 0
-          const float x1 = __builtin_amdgcn_exp2f(t[2 * h + 1] + off);
-          xs += x0 + x1;
-          const __bf16 b0 = (__bf16)x0, b1 = (__bf16)x1;
-          ps += (float)b0 + (float)b1;
-          pw[h] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        }
-        xs = group_sum4(xs);
-        ps = group_sum4(ps);
-        const int row = (qw * kQKT + k) * kTileRows + l16;
-        *(uint2*)(sm.ptile[st & 1] + row * kPRowB + 16 * g + 8 * tt) = make_uint2(pw[0], pw[1]);
-        if (g == 0) ((float*)&sm.cl[st & 1][row])[tt] = c;
-        const float mn = fmaxf(m_run[k], c);
-        const float a = pow2_diff(m_run[k], mn), wt = pow2_diff(c, mn);
-        l_run[k] = l_run[k] * a + xs * wt;
-        lt_run[k] = lt_run[k] * a + ps * wt;
-        m_run[k] = mn;
+        for (int jj = 0; jj < 4; ++jj) x[k][tt][jj] = t[k][tt][jj] + off;
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) x[k][tt][jj] = __builtin_amdgcn_exp2f(x[k][tt][jj]);  // exp2(-inf) = 0
+        xsum[k][tt] = (x[k][tt][0] + x[k][tt][1]) + (x[k][tt][2] + x[k][tt][3]);
       }
+    };
+    // token tile 0
+    kload(0, 0, kf[0]);
+    kload(0, 1, kf[1]);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      if (kk + 2 < kKSteps) kload(0, kk + 2, kf[(kk + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_kk(0, kk);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // token tile 1, with slices of token tile 0's softmax from dot-product step 2 on
+    kload(1, 0, kf[0]);
+    kload(1, 1, kf[1]);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      if (kk + 2 < kKSteps) kload(1, kk + 2, kf[(kk + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_kk(1, kk);
+      const int sl = kk - 2;
+      if (sl >= 0 && sl < 4 * kQKT) part1(sl / 4, 0, sl % 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+      for (int k = 0; k < kQKT; ++k) part1(k, 1, sl);
+    // second half: the new running maximum m, P~ = BF16(x 2^(c - m)), sums, rescale
+#pragma unroll
+    for (int k = 0; k < kQKT; ++k) {
+      const float mn = fmaxf(m_run[k], fmaxf(c[k][0], c[k][1]));
+      const float al = mn == m_run[k] ? 1.f : pow2_diff(m_run[k], mn);  // 1: O unchanged
+      const int row = (qw * kQKT + k) * kTileRows + l16;
+      float xs = 0.f, ps = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const float sc = pow2_diff(c[k][tt], mn);  // 2^(c - m), exact
+        const v2bf p0 = __builtin_convertvector((v2f){x[k][tt][0] * sc, x[k][tt][1] * sc}, v2bf);
+        const v2bf p1 = __builtin_convertvector((v2f){x[k][tt][2] * sc, x[k][tt][3] * sc}, v2bf);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(p0, ones, ps, false);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(p1, ones, ps, false);
+        xs += xsum[k][tt] * sc;
+        *(uint2*)(sm.ptile[st & 1] + row * kPRowB + 16 * g + 8 * tt) =
+            make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+      }
+      xs = group_sum4(xs);
+      ps = group_sum4(ps);
+      if (g == 0) sm.alpha[st & 1][row] = al;
+      l_run[k] = l_run[k] * al + xs;
+      lt_run[k] = lt_run[k] * al + ps;
+      m_run[k] = mn;
+    }
+    stage_off = stage_off == (kStages - 1) * kPageB ? 0 : stage_off + kPageB;
+  };
+  auto qk = [&](int st) {
+    if ((p_first + st) * kPage + kPage > lim_all) qk_step(st, std::true_type{});
+    else qk_step(st, std::false_type{});
   };
 
   __builtin_amdgcn_s_setprio(2);  // the QK waves pace the step: issue first on their SIMD
   block_sync_lds();               // step 0 landed
-  if (nsteps > 0) qk_step(0);
+  if (nsteps > 0) qk(0);
   for (int st = 0; st < nsteps; ++st) {
     block_sync_lds();
-    if (st + 1 < nsteps) qk_step(st + 1);
+    if (st + 1 < nsteps) qk(st + 1);
   }
 
-  // (m, l, l~) of rows 2 qw 16 + 16 k + l16; m is the maximum the PV waves scale O to
+  // (m, l, l~) of rows 2 qw 16 + 16 k + l16; m is the maximum O is scaled to
   if (g == 0) {
     const int64_t part_row0 = (int64_t)it.part * P.rows;
 #pragma unroll
@@ -308,7 +366,7 @@ template <int NT>
 __device__ __forceinline__ void bw_pv(const BWItem& it, BWSmem<NT>& sm) {
   using R = BWRoles<NT>;
   constexpr int kRT = R::kPVT;  // row tiles per PV wave
-  constexpr int kDT = 16;          // 16-dim tiles per PV wave
+  constexpr int kDT = 16;       // 16-dim tiles per PV wave
   constexpr int kDMA = R::kDMA;
   const PlanDev& P = *it.P;
   const int g = it.g, l16 = it.l16, lane = it.lane;
@@ -319,128 +377,117 @@ __device__ __forceinline__ void bw_pv(const BWItem& it, BWSmem<NT>& sm) {
 
   // Direct-to-LDS loads k = pv kDMA + i of a step: LDS bytes [1024 k, 1024 k + 1024) of
   // the stage; lane i fills 16-byte slot s = 64 k + i, which holds chunk
-  // (s % 72 - rot(s / 72)) mod 72 of token row s / 72. Offsets are recomputed at each
-  // issue (the asm keeps the compiler from keeping them live across the loop).
-  auto src_off = [&](int k) -> uint32_t {
-    int ln = lane;
-    __asm__ volatile("" : "+v"(ln));
-    const int slot = k * 64 + ln;
+  // (s % 72 - rot(s / 72)) mod 72 of token row s / 72.
+  uint32_t doff[kDMA];
+#pragma unroll
+  for (int i = 0; i < kDMA; ++i) {
+    const int slot = (pv * kDMA + i) * 64 + lane;
     const int n = slot / kChunks, pos = slot - n * kChunks;
     int c = pos - rot_of(n);
     if (c < 0) c += kChunks;
-    return (uint32_t)(n * kRowB + 16 * c);
-  };
-  auto issue = [&](int st, int64_t id) {
-    const uint64_t gp = uniform_addr(it.kv + id * kPageB);
-    uint8_t* stage = sm.pages[st % kStages];
-#pragma unroll
-    for (int i = 0; i < kDMA; ++i) {
-      const int k = pv * kDMA + i;
-      dma16(gp, src_off(k), (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + k * 1024));
-    }
+    doff[i] = (uint32_t)(n * kRowB + 16 * c);
+  }
+  const uint32_t pages0 = lds_addr(sm.pages[0]);
+  auto issue_one = [&](uint64_t gp, uint32_t stage_base, int i) {
+    dma16(gp, doff[i], stage_base + (uint32_t)((pv * kDMA + i) * 1024));
   };
   auto page_id = [&](int st) -> int64_t { return it.btb[min(p_first + st, p_end - 1)]; };
+  auto stage_of = [&](int st) -> uint32_t { return pages0 + (uint32_t)((st % kStages) * kPageB); };
+  // rows past the split's end (the tail of its last page) read as zero V
+  auto zero_tail = [&](int st) {
+    const int valid = t1 - (p_first + st) * kPage;
+    if (valid >= kPage) return;
+    uint8_t* stage = sm.pages[st % kStages];
+    for (int off = valid * kRowB + 16 * (pv * 64 + lane); off < kPageB; off += 16 * 64 * R::kPVW)
+      *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
+  };
 
   v4f acc[kRT][kDT];
-  float m_c[kRT][4];  // running max of result rows 4 g + jj
-  float m_a[kRT];     // running max of operand row l16
 #pragma unroll
-  for (int k = 0; k < kRT; ++k) {
-    m_a[k] = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) m_c[k][jj] = -INFINITY;
+  for (int k = 0; k < kRT; ++k)
 #pragma unroll
     for (int d = 0; d < kDT; ++d) acc[k][d] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
   // transposed V reads: lane (16 G + u), read r addresses token 16 r + 4 G + u / 4 and
   // dims 16 D + 4 (u % 4) .. + 3 (chunk 2 D + (u % 4) / 2, rotated, never wrapping);
   // lane 16 G + u receives dim 16 D + u of tokens 16 r + 4 G .. 16 r + 4 G + 3
-  int tr_base[2];
+  uint32_t tr_base[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int t = 16 * r + 4 * g + (l16 >> 2);
-    tr_base[r] = t * kRowB + 16 * (((l16 & 3) >> 1) + rot_of(t)) + 8 * (l16 & 1) + 512 * dh;
+    tr_base[r] = (uint32_t)(t * kRowB + 16 * (((l16 & 3) >> 1) + rot_of(t)) + 8 * (l16 & 1) +
+                            512 * dh);
   }
 
-  auto pv_step = [&](int st) {
-    const uint8_t* stage = sm.pages[st % kStages];
+  // one step: rescale O where a row's maximum moved, O += P~ V over the stage's page,
+  // with the direct-to-LDS loads of step st + 3 (when dma) issued between the MFMAs
+  auto pv_step = [&](int st, bool dma, uint64_t gp) {
     const int pb = st & 1;
     v8bf pa[kRT];
 #pragma unroll
     for (int k = 0; k < kRT; ++k) {
       const int rt = rt0 + k;
-      bool rescale = false;
-      float alpha[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float2 cc = sm.cl[pb][rt * kTileRows + 4 * g + jj];
-        const float mn = fmaxf(m_c[k][jj], fmaxf(cc.x, cc.y));
-        alpha[jj] = mn == m_c[k][jj] ? 1.f : pow2_diff(m_c[k][jj], mn);
-        rescale |= mn != m_c[k][jj];
-        m_c[k][jj] = mn;
-      }
-      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+      const float4 al = *(const float4*)&sm.alpha[pb][rt * kTileRows + 4 * g];
+      if (__builtin_amdgcn_ballot_w64(al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f) != 0) {
 #pragma unroll
         for (int d = 0; d < kDT; ++d) {
-          acc[k][d][0] *= alpha[0]; acc[k][d][1] *= alpha[1];
-          acc[k][d][2] *= alpha[2]; acc[k][d][3] *= alpha[3];
+          acc[k][d][0] *= al.x; acc[k][d][1] *= al.y;
+          acc[k][d][2] *= al.z; acc[k][d][3] *= al.w;
         }
       }
-      // operand row l16: tile tt's P~ times 2^(c_tt - m)
-      const float2 ca = sm.cl[pb][rt * kTileRows + l16];
-      m_a[k] = fmaxf(m_a[k], fmaxf(ca.x, ca.y));
-      const float s0 = pow2_diff(ca.x, m_a[k]), s1 = pow2_diff(ca.y, m_a[k]);
-      v4i pw = ld16(sm.ptile[pb], (rt * kTileRows + l16) * kPRowB + 16 * g);
-      if (__builtin_amdgcn_ballot_w64(s0 != 1.f || s1 != 1.f) != 0) {
-        pw.x = (int)scale_bf16x2((uint32_t)pw.x, s0);
-        pw.y = (int)scale_bf16x2((uint32_t)pw.y, s0);
-        pw.z = (int)scale_bf16x2((uint32_t)pw.z, s1);
-        pw.w = (int)scale_bf16x2((uint32_t)pw.w, s1);
-      }
-      pa[k] = as_bf8(pw);
+      pa[k] = as_bf8(ld16(sm.ptile[pb], (rt * kTileRows + l16) * kPRowB + 16 * g));
     }
-    // tokens past the split's end may hold poison: zero their V elements (P~ is 0)
-    uint32_t mk[2][2] = {{0xFFFFFFFFu, 0xFFFFFFFFu}, {0xFFFFFFFFu, 0xFFFFFFFFu}};
-    if (st == nsteps - 1) {
-      const int valid = t1 - (p_first + st) * kPage;
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int tk = 16 * r + 4 * g + 2 * h;
-          mk[r][h] = (tk < valid ? 0x0000FFFFu : 0u) | (tk + 1 < valid ? 0xFFFF0000u : 0u);
-        }
-    }
+    const uint32_t sb = stage_of(st);
+    const uint32_t dst = stage_of(st + 3);
+    const uint32_t v0 = sb + tr_base[0], v1 = sb + tr_base[1];
+    v4s vr[3][2];
+    auto vload = [&](int d, v4s (&f)[2]) {
+      f[0] = lds_tr16(v0 + 32 * d);
+      f[1] = lds_tr16(v1 + 32 * d);
+    };
+    vload(0, vr[0]);
+    vload(1, vr[1]);
 #pragma unroll
     for (int d = 0; d < kDT; ++d) {
-      const v4s b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(stage + tr_base[0] + 32 * d));
-      const v4s b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4s*)(stage + tr_base[1] + 32 * d));
-      const v2u x0 = __builtin_bit_cast(v2u, b0);
-      const v2u x1 = __builtin_bit_cast(v2u, b1);
-      const v4i vb = v4i{(int)(x0.x & mk[0][0]), (int)(x0.y & mk[0][1]),
-                         (int)(x1.x & mk[1][0]), (int)(x1.y & mk[1][1])};
+      if (d + 2 < kDT) vload(d + 2, vr[(d + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      const v2u x0 = __builtin_bit_cast(v2u, vr[d % 3][0]);
+      const v2u x1 = __builtin_bit_cast(v2u, vr[d % 3][1]);
+      const v4i vb = v4i{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y};
 #pragma unroll
       for (int k = 0; k < kRT; ++k)
         acc[k][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[k], as_bf8(vb), acc[k][d], 0, 0, 0);
+      if (d < kDMA && dma) issue_one(gp, dst, d);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- pipeline: 1 + nsteps barriers, like the QK waves; a step's page id is read one
   // step before its loads are issued
   int64_t nid = 0;
-  if (nsteps > 0) issue(0, page_id(0));
-  if (nsteps > 1) issue(1, page_id(1));
-  if (nsteps > 2) nid = page_id(2);
-  if (nsteps > 1) wait_vmcnt<kDMA>(); else wait_vmcnt<0>();  // step 0 landed
-  block_sync_lds();
-  for (int st = 0; st < nsteps; ++st) {
-    wait_vmcnt<0>();  // step st + 1 landed
-    block_sync_lds();
-    if (st + 2 < nsteps) {
-      issue(st + 2, nid);
-      if (st + 3 < nsteps) nid = page_id(st + 3);
+#pragma unroll
+  for (int pre = 0; pre < kStages - 1; ++pre) {
+    if (pre < nsteps) {
+      const uint64_t gp = uniform_addr(it.kv + page_id(pre) * kPageB);
+#pragma unroll
+      for (int i = 0; i < kDMA; ++i) issue_one(gp, stage_of(pre), i);
     }
-    pv_step(st);
+  }
+  if (nsteps > kStages - 1) nid = page_id(kStages - 1);
+  // step 0 landed: the loads of steps 1 and 2 may still be in flight
+  if (nsteps > 2) wait_vmcnt<2 * kDMA>();
+  else if (nsteps > 1) wait_vmcnt<kDMA>();
+  else wait_vmcnt<0>();
+  block_sync_lds();
+  if (nsteps == 1) zero_tail(0);
+  for (int st = 0; st < nsteps; ++st) {
+    // step st + 1 landed; step st + 2's loads may stay in flight
+    if (st + 2 < nsteps) wait_vmcnt<kDMA>(); else wait_vmcnt<0>();
+    block_sync_lds();
+    if (st + 2 == nsteps) zero_tail(st + 1);
+    const bool dma = st + 3 < nsteps;
+    const uint64_t gp = uniform_addr(it.kv + nid * kPageB);
+    if (dma && st + 4 < nsteps) nid = page_id(st + 4);
+    pv_step(st, dma, gp);
   }
 
   // ---- partials: O rows rt 16 + 4 g + jj, dims 256 dh + 16 d + l16
