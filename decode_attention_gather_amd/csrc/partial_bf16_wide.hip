@@ -19,11 +19,13 @@
 //  * Gather: direct-to-LDS loads (global_load_lds_dwordx4, 1 KB per instruction) of one
 //    page (36 KB) per pipeline step into a 4-stage ring (160 KB of LDS with P~), issued
 //    by the PV waves three steps ahead between their MFMAs, so a load has two steps to
-//    land. Rows stay 1152 bytes; 16-byte chunk c of token
-//    row n sits at chunk (c + ((n >> 1) & 7)) mod 72, which puts the 16 rows of an
-//    operand read on distinct LDS banks (a row is 288 dwords, so consecutive rows start
-//    half of the 64 banks apart, and the rotation spreads 8 row pairs over the other
-//    offsets). Rows past the split's end are zeroed in LDS once, so V needs no mask.
+//    land. Rows stay 1152 bytes; 16-byte chunk c of token row n sits at chunk
+//    (c + rot(n)) mod 72 with rot(n) = 2 ((n >> 1) & 3) + ((n >> 3) & 1). A row is 288
+//    dwords, so consecutive rows start half of the 64 banks apart; the rotation then
+//    puts the 16 rows of a K operand read (16 bytes per lane) on 16 distinct 4-bank
+//    groups, and the 8 tokens that one pass of a transposed V read serves (32 bytes
+//    each) on 8 distinct 8-bank groups. Rows past the split's end are zeroed in LDS
+//    once, so V needs no mask.
 //  * QK^T: NT/2 QK waves; wave q holds Q^T of row tiles 2q, 2q + 1 (144 VGPRs: BF16
 //    Q^T of three tiles would not fit beside the accumulators) and forms S^T = K Q^T of
 //    both 16-token tiles of the page on v_mfma_f32_16x16x32_bf16, K fragments read two
@@ -91,7 +93,8 @@ struct __attribute__((aligned(16))) BWSmem {
   float alpha[2][NT * kTileRows];             // per row: 2^(m_old - m_new) of the step
 };
 
-__device__ __forceinline__ int rot_of(int n) { return (n >> 1) & 7; }
+// Chunk rotation of token row n (see the layout note at the top).
+__device__ __forceinline__ int rot_of(int n) { return 2 * ((n >> 1) & 3) + ((n >> 3) & 1); }
 
 __device__ __forceinline__ v4i ld16(const uint8_t* base, int off) {
   return *(const v4i*)(base + off);
@@ -227,7 +230,7 @@ __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
   }
 
   // K operand of token row n = 16 tt + l16: chunk 4 kk + g at (4 kk + g + rot(n)) mod 72;
-  // rot(n) = (l16 >> 1) & 7 for both tiles. Latent steps (kk < 16) never wrap.
+  // rot(16 + l16) = rot(l16). Latent steps (kk < 16) never wrap.
   const int rot = rot_of(l16);
   const uint32_t pages0 = lds_addr(sm.pages[0]);
   const uint32_t k_lat = pages0 + l16 * kRowB + 16 * (g + rot);
