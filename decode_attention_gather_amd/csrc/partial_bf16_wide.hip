@@ -149,11 +149,12 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
+// (IEEE maximum: one v_maximum3_f32, where fmaxf would first quiet both swapped values)
 __device__ __forceinline__ float group_max4(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float m = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_sum4(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -139,17 +139,27 @@ __device__ __forceinline__ v4i ld16(const uint8_t* base, int off) {
   return *(const v4i*)(base + off);
 }
 
+// LDS byte address of a shared-memory pointer, and a transposed read from such an
+// address (a constant added to one base register becomes the instruction's offset).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS uint8_t*)p;
+}
+__device__ __forceinline__ v2i lds_tr8(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(uintptr_t)a);
+}
+
 __device__ __forceinline__ v8i cat8(v4i a, v4i b) {
   return v8i{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
 // Max / sum over the four 16-lane groups (lanes l, l ^ 16, l ^ 32, l ^ 48) with the
 // VALU lane swaps of gfx950 instead of LDS permutes.
+// (IEEE maximum: one v_maximum3_f32, where fmaxf would first quiet both swapped values)
 __device__ __forceinline__ float group_max4(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float m = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_sum4(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -424,15 +434,25 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     const int pa = p_first + st * kStepPages;
     return ld_page_b ? min(pa + 1, p_end - 1) : pa;
   };
+  const uint32_t pages0 = lds_addr(sm.pages[0]);
+  auto stage_of = [&](int st) -> uint32_t { return pages0 + (uint32_t)((st % kStages) * kStepBytes); };
+  auto issue_one = [&](uint64_t gp, uint32_t stage_base, int i) {
+    const uint32_t off = (src2[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+    dma16(gp, off, stage_base + (uint32_t)((pv * R::kDMA + i) * 1024));
+  };
   auto issue = [&](int st, int64_t id) {
     const uint64_t gp = uniform_addr(it.kv + id * kPageBytes);
-    uint8_t* stage = sm.pages[st % kStages];
 #pragma unroll
-    for (int i = 0; i < R::kDMA; ++i) {
-      const int k = pv * R::kDMA + i;
-      const uint32_t off = (src2[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-      dma16(gp, off, (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + k * 1024));
-    }
+    for (int i = 0; i < R::kDMA; ++i) issue_one(gp, stage_of(st), i);
+  };
+  // token rows of a step past the split's end (its last step) read as zero V: the
+  // stage holds the step's 64 token rows back to back
+  auto zero_tail = [&](int st) {
+    const int valid = t1 - (p_first + st * kStepPages) * kPage;
+    if (valid >= kStepPages * kPage) return;
+    uint8_t* stage = sm.pages[st % kStages];
+    for (int off = valid * kDQK + 16 * (pv * 64 + lane); off < kStepBytes; off += 16 * 64 * R::kPVW)
+      *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
   };
 
   v4f acc[kRT][kDT];
@@ -451,8 +471,9 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     tr_base[r] = (g >> 1) * kPageBytes + t * kDQK + 16 * (kDT * dh + rot_of(t)) + 8 * (l16 & 1);
   }
 
-  auto pv_step = [&](int st) {
-    const uint8_t* stage = sm.pages[st % kStages];
+  // one step: O += P~ V over the stage's two pages, with the direct-to-LDS loads of
+  // step st + 2 (when dma) issued between the MFMAs
+  auto pv_step = [&](int st, bool dma, uint64_t gp) {
     const int pb = st & 1;
     int sa[kRT];
     v8i pa[kRT];
@@ -506,28 +527,19 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
         acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[k], ones, acc1, 0, 0, 0, sa[k], 0, 127);
       }
     }
-    // bytes of tokens past the split's end may be poison: zero them (P~ is 0 there).
-    // Byte j of word w of the V operand is step token 32 (g >> 1) + 16 (w >> 1) +
-    // 8 (g & 1) + 4 (w & 1) + j.
-    uint32_t mk[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-    if (st == nsteps - 1) {
-      const int valid = t1 - (p_first + st * kStepPages) * kPage;
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        // the first nb bytes of the word are valid
-        const int nb = min(max(valid - (32 * (g >> 1) + 16 * (wd >> 1) + 8 * (g & 1) + 4 * (wd & 1)), 0), 4);
-        mk[wd] = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
-      }
-    }
+    // V: byte j of word w of the operand is step token 32 (g >> 1) + 16 (w >> 1) +
+    // 8 (g & 1) + 4 (w & 1) + j; rows past the split's end were zeroed in LDS
+    const uint32_t sb = stage_of(st), dst = stage_of(st + 2);
+    const uint32_t v0 = sb + tr_base[0], v1 = sb + tr_base[1];
 #pragma unroll
     for (int d = 0; d < kDT; ++d) {
-      const v2i b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[0] + 16 * d));
-      const v2i b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i*)(stage + tr_base[1] + 16 * d));
-      const int x0 = b0.x & mk[0], x1 = b0.y & mk[1], x2 = b1.x & mk[2], x3 = b1.y & mk[3];
-      const v8i vb = v8i{x0, x1, x2, x3, x0, x1, x2, x3};
+      const v2i b0 = lds_tr8(v0 + 16 * d);
+      const v2i b1 = lds_tr8(v1 + 16 * d);
+      const v8i vb = v8i{b0.x, b0.y, b1.x, b1.y, b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
       for (int k = 0; k < kRT; ++k)
         acc[k][d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[k], vb, acc[k][d], 0, 0, 0, sa[k], 0, 127);
+      if (d < R::kDMA && dma) issue_one(gp, dst, d);
     }
   };
 
@@ -539,14 +551,15 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   if (nsteps > 2) nid = it.btb[page_of(2)];
   if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // step 0 landed
   block_sync_lds();
+  if (nsteps == 1) zero_tail(0);
   for (int st = 0; st < nsteps; ++st) {
     wait_vmcnt<0>();  // step st + 1 landed
     block_sync_lds();
-    if (st + 2 < nsteps) {
-      issue(st + 2, nid);
-      if (st + 3 < nsteps) nid = it.btb[page_of(st + 3)];
-    }
-    pv_step(st);
+    if (st + 2 == nsteps) zero_tail(st + 1);
+    const bool dma = st + 2 < nsteps;
+    const uint64_t gp = uniform_addr(it.kv + nid * kPageBytes);
+    if (dma && st + 3 < nsteps) nid = it.btb[page_of(st + 3)];
+    pv_step(st, dma, gp);
   }
 
   // ---- O partial rows rt 16 + 4 g + jj, dims 256 dh + 16 d + l16

@@ -92,6 +92,19 @@ def test_bf16_split_invariance_f32(mla, q_len):
         np.testing.assert_allclose(lse, outs[0][1], rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("heads,q_len", [(12, 8), (12, 4), (16, 7), (12, 1)])
+def test_bf16_determinism(mla, heads, q_len):
+    """Repeated calls give the same bits (wide blocks of 6 and 4 row tiles, narrow)."""
+    case = inputs.make_case([4096, 777], num_heads=heads, q_len=q_len, seed=19, split_kv=3,
+                            kv_dtype="bf16")
+    dc = mla.to_device(case)
+    _say(f"[gpu] bf16 determinism H={heads} q={q_len}")
+    o1, l1, _ = run_bf16(mla, case, dc=dc)
+    for _ in range(2):
+        o2, l2, _ = run_bf16(mla, case, dc=dc)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_bf16_graph_equals_host_and_varq(mla):
     lens = [3000, 777, 64]
     case = inputs.make_case(lens, num_heads=12, q_len=4, seed=9004, kv_dtype="bf16")

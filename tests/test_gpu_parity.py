@@ -141,13 +141,16 @@ def test_split_invariance_f32(mla):
         assert dl <= 1e-5 * max(1.0, float(np.abs(base[2]).max())), (sk, dl)
 
 
-def test_determinism(mla):
-    case = inputs.make_case([4096, 777], num_heads=12, q_len=8, seed=9, split_kv=3)
+@pytest.mark.parametrize("heads,q_len", [(12, 8), (12, 4), (16, 4), (12, 1)])
+def test_determinism(mla, heads, q_len):
+    """Repeated calls give the same bits (wide blocks of 6 and 4 row tiles, narrow)."""
+    case = inputs.make_case([4096, 777], num_heads=heads, q_len=q_len, seed=9, split_kv=3)
     dc = mla.to_device(case)
-    _say("[gpu] determinism")
+    _say(f"[gpu] determinism H={heads} q={q_len}")
     o1, l1, _ = run_gpu(mla, case, dc=dc)
-    o2, l2, _ = run_gpu(mla, case, dc=dc)
-    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    for _ in range(2):
+        o2, l2, _ = run_gpu(mla, case, dc=dc)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_device_lengths_shorter_than_plan(mla):
