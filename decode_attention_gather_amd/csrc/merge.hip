@@ -2,10 +2,13 @@
 //
 // Method of TensorRT-LLM PR #20380 "trtllm-gen FMHA: split the KV partials of a row
 // across thread groups in fmhaReductionKernel" (Description), re-done for 64-wide
-// wavefronts: one workgroup per row with G wavefront groups; group g folds partials
-// g, g + G, ... with the online-softmax merge, then the groups are combined through LDS,
-// each scaled by 2^(group max - max) and empty groups skipped. Each lane owns 8 of the
-// 512 output dims, so every partial row is one fully coalesced 2 KB read per wavefront.
+// wavefronts: W workgroups per row (W = 1, 2, 4 or 8, each owning 512 / W of the output
+// dims) with G wavefront groups each; group g folds partials g, g + G, ... with the
+// online-softmax merge, then the groups are combined through LDS, each scaled by
+// 2^(group max - max) and empty groups skipped. A lane owns 8 / W consecutive dims, so
+// every partial row is one fully coalesced read of 2 KB / W per wavefront. W = 8 only
+// when very few rows hold many splits (one long request): then a workgroup per row
+// would leave most CUs idle while each of its waves walks its partials in rounds.
 //
 // Partials arrive from the split-KV kernel as (m, l, l~, O) with m an integer (log2
 // units), so every rescale here is an exact power of two (v_ldexp_f32):
@@ -69,7 +72,7 @@ struct MergeSmem {
 };
 
 // kDev: the plan and output_scale come from device memory (graph path).
-template <bool kF32Out, bool kDev>
+template <bool kF32Out, bool kDev, int kW>
 __global__ void __launch_bounds__(64 * kMaxGroups)
 merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
              const float* __restrict__ oscale_dev, const float* __restrict__ ws_o,
@@ -78,52 +81,70 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   __shared__ MergeSmem sm;
   const PlanDev& P = kDev ? *pdev : Parg;
   const float output_scale = kDev ? *oscale_dev : output_scale_arg;
+  constexpr int kD = 8 / kW;                  // dims per lane
+  constexpr int kSlice = kDV / kW;            // dims per workgroup
+  // partials in flight per wavefront (4 at W = 1: more registers would halve the
+  // workgroups a CU holds, which costs more than the extra loads give)
+  constexpr int kU = kW >= 2 ? 16 : 4;
   // groups in use: the launch's, or the device plan's (<= the launch's) on the graph path
   const int G = kDev ? min(P.groups, groups) : groups;
-  const int row_global = blockIdx.x;  // (b * q_len + j) * H + h
+  const int row_global = blockIdx.x / kW;  // (b * q_len + j) * H + h
+  const int dim0 = (blockIdx.x - row_global * kW) * kSlice;
   const int b = row_global / P.rows;
   const int r = row_global - b * P.rows;
   const int S = P.splits[b];
   const int base = (int)P.part_base[b];
   const int lane = threadIdx.x & 63;
-  const int gw = threadIdx.x >> 6;
+  const int gw = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
   float M = -INFINITY, l = 0.f, lt = 0.f;
-  float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-  for (int s0 = gw; gw < G && s0 < S; s0 += kUnroll * G) {
-    float4 stv[kUnroll], a[kUnroll], c[kUnroll];
+  float o[kD];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+  for (int i = 0; i < kD; ++i) o[i] = 0.f;
+  for (int s0 = gw; gw < G && s0 < S; s0 += kU * G) {
+    float4 stv[kU];
+    float a[kU][kD];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
       const int s = s0 + u * G;
       if (s < S) {
         const int64_t pr = (int64_t)(base + s) * P.rows + r;
         stv[u] = *(const float4*)(ws_stats + pr * kStatStride);
-        const float4* op = (const float4*)(ws_o + pr * kDV) + 2 * lane;
-        a[u] = op[0];
-        c[u] = op[1];
+        const float* op = ws_o + pr * kDV + dim0 + kD * lane;
+        if constexpr (kD == 8) {
+          const float4 x = ((const float4*)op)[0], y = ((const float4*)op)[1];
+          a[u][0] = x.x; a[u][1] = x.y; a[u][2] = x.z; a[u][3] = x.w;
+          a[u][4] = y.x; a[u][5] = y.y; a[u][6] = y.z; a[u][7] = y.w;
+        } else if constexpr (kD == 4) {
+          const float4 x = *(const float4*)op;
+          a[u][0] = x.x; a[u][1] = x.y; a[u][2] = x.z; a[u][3] = x.w;
+        } else if constexpr (kD == 2) {
+          const float2 x = *(const float2*)op;
+          a[u][0] = x.x; a[u][1] = x.y;
+        } else {
+          a[u][0] = *op;
+        }
       } else {
         stv[u] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-        a[u] = c[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < kD; ++i) a[u][i] = 0.f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const float ms = stv[u].x;
       if (ms == -INFINITY) continue;
       const float Mn = fmaxf(M, ms);
       const float wa = pow2i(M, Mn), wb = pow2i(ms, Mn);
-      o0.x = o0.x * wa + a[u].x * wb; o0.y = o0.y * wa + a[u].y * wb;
-      o0.z = o0.z * wa + a[u].z * wb; o0.w = o0.w * wa + a[u].w * wb;
-      o1.x = o1.x * wa + c[u].x * wb; o1.y = o1.y * wa + c[u].y * wb;
-      o1.z = o1.z * wa + c[u].z * wb; o1.w = o1.w * wa + c[u].w * wb;
+#pragma unroll
+      for (int i = 0; i < kD; ++i) o[i] = o[i] * wa + a[u][i] * wb;
       l = l * wa + stv[u].y * wb;
       lt = lt * wa + stv[u].z * wb;
       M = Mn;
     }
   }
-  float4* so = (float4*)sm.o[gw] + 2 * lane;
-  so[0] = o0;
-  so[1] = o1;
+#pragma unroll
+  for (int i = 0; i < kD; ++i) sm.o[gw][kD * lane + i] = o[i];
   if (lane == 0) {
     sm.m[gw] = M;
     sm.l[gw] = l;
@@ -150,25 +171,26 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   }
   const float inv = Lt > 0.f ? output_scale / Lt : 0.f;
   if (kF32Out || ep.o_fp8 == nullptr) {
-    for (int d = threadIdx.x; d < kDV; d += blockDim.x) {
+    for (int d = threadIdx.x; d < kSlice; d += blockDim.x) {
       float acc = 0.f;
       for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d];
       const float v = acc * inv;
       if (kF32Out)
-        ((float*)out)[(int64_t)row_global * kDV + d] = v;
+        ((float*)out)[(int64_t)row_global * kDV + dim0 + d] = v;
       else
-        ((uint16_t*)out)[(int64_t)row_global * kDV + d] = f32_to_bf16_rne(v);
+        ((uint16_t*)out)[(int64_t)row_global * kDV + dim0 + d] = f32_to_bf16_rne(v);
     }
-  } else if (threadIdx.x < 64) {
-    // MXFP8 (and BF16 when out is given): lane t owns dims 8t .. 8t + 7
-    const int d0 = 8 * (int)threadIdx.x;
+  } else if (threadIdx.x < kSlice / 8) {
+    // MXFP8 (and BF16 when out is given): lane t owns dims dim0 + 8t .. dim0 + 8t + 7
+    const int dl = 8 * (int)threadIdx.x;  // in the slice (sm.o)
+    const int d0 = dim0 + dl;             // in the row
     float vb[8];
     uint32_t hw[4];
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float acc = 0.f;
-      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d0 + i];
+      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][dl + i];
       const uint16_t h16 = f32_to_bf16_rne(acc * inv);
       vb[i] = __uint_as_float((uint32_t)h16 << 16);
       amax = fmaxf(amax, fabsf(vb[i]));
@@ -193,9 +215,9 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                                          __builtin_amdgcn_ldexpf(vb[7], -e), c1, true);
     *(uint2*)(ep.o_fp8 + (int64_t)row_global * kDV + d0) = make_uint2((uint32_t)c0, (uint32_t)c1);
     if ((threadIdx.x & 3) == 0)
-      ep.o_fp8_scales[(int64_t)row_global * (kDV / 32) + (threadIdx.x >> 2)] = (uint8_t)(e + 127);
+      ep.o_fp8_scales[(int64_t)row_global * (kDV / 32) + (d0 >> 5)] = (uint8_t)(e + 127);
   }
-  if (lse != nullptr && threadIdx.x == 0)
+  if (lse != nullptr && dim0 == 0 && threadIdx.x == 0)
     lse[row_global] = L > 0.f ? 0.69314718055994531f * ((Mx - 8.f) + log2f(L)) : -INFINITY;
 }
 
@@ -211,18 +233,25 @@ int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* 
   const float* od = dev ? dev->output_scale : nullptr;
   const MergeEpilogue ep = epi ? *epi : MergeEpilogue{nullptr, nullptr, nullptr};
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(rows_total), block(64 * groups);
-  if (o_is_f32) {
-    if (dev)
-      hipLaunchKernelGGL((merge_kernel<true, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
-    else
-      hipLaunchKernelGGL((merge_kernel<true, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
-  } else {
-    if (dev)
-      hipLaunchKernelGGL((merge_kernel<false, true>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
-    else
-      hipLaunchKernelGGL((merge_kernel<false, false>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep);
+  const int W = plan.merge_slices;
+  const dim3 grid(rows_total * W), block(64 * groups);
+  // one instantiation per (output type, plan source, slices)
+#define MLA_MERGE_LAUNCH(F32, DEV, KW) \
+  hipLaunchKernelGGL((merge_kernel<F32, DEV, KW>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep)
+#define MLA_MERGE_W(F32, DEV)                      \
+  switch (W) {                                     \
+    case 1: MLA_MERGE_LAUNCH(F32, DEV, 1); break;  \
+    case 2: MLA_MERGE_LAUNCH(F32, DEV, 2); break;  \
+    case 4: MLA_MERGE_LAUNCH(F32, DEV, 4); break;  \
+    default: MLA_MERGE_LAUNCH(F32, DEV, 8); break; \
   }
+  if (o_is_f32) {
+    if (dev) { MLA_MERGE_W(true, true) } else { MLA_MERGE_W(true, false) }
+  } else {
+    if (dev) { MLA_MERGE_W(false, true) } else { MLA_MERGE_W(false, false) }
+  }
+#undef MLA_MERGE_W
+#undef MLA_MERGE_LAUNCH
   return (int)hipGetLastError();
 }
 

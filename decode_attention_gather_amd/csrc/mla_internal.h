@@ -25,6 +25,7 @@ constexpr int kMaxBatch = MLA_MAX_BATCH;
 constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
 constexpr int kMergeWavesPerCu = 32;      // merge launch budget: waves resident per CU
+constexpr int kMaxMergeSlices = 8;         // merge: at most 8 workgroups per row
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroup i runs on XCD i mod 8
 
 // Everything the kernels need from a plan, passed by value as a kernel argument
@@ -69,6 +70,7 @@ struct mla_decode_plan_s {
   int32_t max_split_kv;   // graph plans: per-request split cap
   size_t ws_plan_bytes;   // graph plans: device PlanDev at the head of the workspace
   int32_t merge_groups;
+  int32_t merge_slices;   // workgroups per row in the merge (1, 2, 4 or 8 dim slices)
   int32_t max_splits;
   int32_t num_cus;
   size_t ws_o_bytes;      // fp32 partial O region

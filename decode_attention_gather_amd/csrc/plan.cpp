@@ -96,6 +96,25 @@ int32_t merge_groups_for(const std::vector<int64_t>& splits, int64_t rows, int32
   return g;
 }
 
+// Merge slices: a row's 512 output dims may be split over W = 8 workgroups. Measured
+// on the merge kernel: more workgroups help only when very few rows hold many splits
+// (one long request at q = 1: 12 rows x 256 splits, 11.1 -> 8.0 us), where each
+// wavefront would otherwise walk its partials in several dependent rounds; elsewhere
+// the extra waves cost more than they give (192 rows x 16 splits: 6.2 -> 7.1 us; a
+// skewed batch: 13.4 -> 50 us). So W = 8 when the rows of the requests with the most
+// splits (S_b at least half the largest) number at most num_cus / 16 and those requests
+// have more than 16 x 8 splits (several rounds per wavefront even at 16 groups); else
+// 1. The slices do not change
+// any sum's order (each dim is still folded by one lane), and the merge width above
+// ignores them, so host and graph plans of the same lengths give the same bits.
+int32_t merge_slices_for(const std::vector<int64_t>& splits, int64_t rows, int32_t num_cus) {
+  int64_t max_s = 0, heavy = 0;
+  for (int64_t sb : splits) max_s = std::max(max_s, sb);
+  for (int64_t sb : splits)
+    if (2 * sb >= max_s) heavy += rows;
+  return (heavy * 16 <= num_cus && max_s > 16 * 8) ? kMaxMergeSlices : 1;
+}
+
 }  // namespace
 
 int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_t num_heads,
@@ -175,6 +194,7 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     d.sorted[e] = (run << 8) | (uint32_t)order[e];
   }
 
+  plan->merge_slices = merge_slices_for(split_of, rows, num_cus);
   plan->merge_groups = merge_groups_for(split_of, rows, num_cus);
   d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)max_s;
@@ -243,6 +263,8 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   plan->kv_lens = nullptr;
   // launch width: the widest merge any lengths can ask for (the device planner applies
   // the budget to the actual splits and picks <= this)
+  // slices as for a batch of equal requests at the largest split count
+  plan->merge_slices = merge_slices_for(std::vector<int64_t>(batch, per_req), rows, num_cus);
   plan->merge_groups = merge_groups_for(std::vector<int64_t>(1, per_req), 0, num_cus);
   d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)per_req;
@@ -309,6 +331,7 @@ int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info
   info->total_splits = d.total_parts;
   info->work_items = d.total_parts * d.tiles;
   info->merge_groups = plan->merge_groups;
+  info->merge_slices = plan->merge_slices;
   info->max_splits = plan->max_splits;
   for (int32_t b = 0; b < d.batch; ++b) {  // graph plans: decided on the device, 0 here
     if (splits) splits[b] = plan->device_lengths ? 0 : d.splits[b];

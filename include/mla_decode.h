@@ -131,6 +131,8 @@ typedef struct {
   int32_t work_items;       /* total_splits * row_tiles */
   int32_t merge_groups;     /* wavefront groups per row in the merge (power of 2) */
   int32_t max_splits;       /* max_b S_b */
+  int32_t merge_slices;     /* workgroups per row in the merge (1, 2, 4 or 8 slices of
+                               the 512 output dims) */
 } mla_decode_plan_info_t;
 
 int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,

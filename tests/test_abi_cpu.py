@@ -104,6 +104,21 @@ def test_planner_proportional_and_cap():
     assert p.info()[1] == [256]
 
 
+def test_merge_slices_rule():
+    """Workgroups per row in the merge: 8 only when the rows of the requests holding the
+    most splits number at most num_cus / 16 and those splits exceed 16 x 8; else 1."""
+    assert plan([1048576], 1, 12, 0, cap=256).info()[0].merge_slices == 8   # 12 rows x 256
+    assert plan([1048576], 1, 12, 100).info()[0].merge_slices == 1          # 100 splits
+    assert plan([1048576], 2, 12, 0, cap=256).info()[0].merge_slices == 1   # 24 rows
+    assert plan([131072] * 16, 1, 12, 0).info()[0].merge_slices == 1
+    assert plan([1 << 20] + [4096] * 7, 8, 12, 0, cap=256).info()[0].merge_slices == 1
+    # graph plans: as for a batch of equal requests at the largest split count
+    g = mla.Plan.graph(1, q_len=1, num_heads=12, max_kv_len=1 << 20, num_cus=256)
+    assert g.info()[0].merge_slices == 8
+    g = mla.Plan.graph(16, q_len=1, num_heads=12, max_kv_len=131072, num_cus=256)
+    assert g.info()[0].merge_slices == 1
+
+
 def test_merge_groups_rule():
     assert plan([1048576], 1, 12, 100).info()[0].merge_groups == 16
     assert plan([2048], 1, 12, 4).info()[0].merge_groups == 4
