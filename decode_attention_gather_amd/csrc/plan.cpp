@@ -49,15 +49,34 @@ void want_splits(const std::vector<int64_t>& pages, int32_t split_kv, int32_t ma
     for (size_t b = 0; b < B; ++b) want[b] = std::min<int64_t>(split_kv, max_split);
     return;
   }
-  // Proportional plan: sum_b S_b ~= the one-wave split budget, S_b proportional to the
-  // pages of request b, so every work item streams about the same number of pages.
-  int64_t total = 0;
-  for (int64_t p : pages) total += p;
-  const double items_per_page = (double)split_budget(num_cus, tiles) / (double)total;
-  for (size_t b = 0; b < B; ++b) {
-    int64_t s = (int64_t)(items_per_page * (double)pages[b]);  // floor: at most one wave
-    want[b] = std::max<int64_t>(1, std::min<int64_t>(s, max_split));
+  // Proportional plan: S_b = ceil(pages_b / C) with C the smallest split length (pages)
+  // for which sum_b clamp(ceil(pages_b / C), 1, cap) fits the one-wave split budget. The
+  // splits follow the lengths, and the rounding keeps the longest split, which the whole
+  // launch waits for, as short as the budget allows (flooring each request's share of
+  // the budget instead can leave one request's splits nearly twice the mean).
+  const int64_t budget = split_budget(num_cus, tiles);
+  int64_t total = 0, max_p = 1;
+  for (int64_t p : pages) {
+    total += p;
+    max_p = std::max(max_p, p);
   }
+  auto count = [&](int64_t C) {
+    int64_t n = 0;
+    for (int64_t p : pages) n += std::min<int64_t>(std::max<int64_t>(ceil_div(p, C), 1), max_split);
+    return n;
+  };
+  // C = max_p gives one split per request; with budget > B, C = ceil(total / (budget - B))
+  // fits as well, since sum_b ceil(p_b / C) < total / C + B
+  const int64_t Bn = (int64_t)B;
+  int64_t lo = 1, hi = max_p;
+  if (budget > Bn) hi = std::min(hi, ceil_div(total, budget - Bn));
+  else lo = hi;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (count(mid) <= budget) hi = mid; else lo = mid + 1;
+  }
+  for (size_t b = 0; b < B; ++b)
+    want[b] = std::min<int64_t>(std::max<int64_t>(ceil_div(pages[b], lo), 1), max_split);
 }
 
 // Row blocks of 16-row MFMA tiles. Up to 32 rows: one block of 1 or 2 tiles (narrow

@@ -10,8 +10,9 @@
 // One workgroup of 256 threads; thread b owns request b:
 //   L_b = clamp(kv_lens[b], 0, max_kv_len), pages_b = ceil(L_b / 32)
 //   wanted splits: the uniform bound min(split_kv, cap), or the one-wave proportional
-//   rule floor(budget pages_b / sum pages) clamped to [1, cap], budget = the host
-//   planner's XCD-aware split budget
+//   rule clamp(ceil(pages_b / C), 1, cap) with C the smallest split length for which
+//   the sum of those fits the host planner's XCD-aware split budget (the same integer
+//   search as the host planner)
 //   S_b = clamp(wanted, 1, max(pages_b, 1)), at least ceil(pages_b / 65535),
 //   chunk_b = ceil(pages_b / S_b) pages, S_b = ceil(pages_b / chunk_b)  (no empty split)
 // then the requests are ranked longest chunk first (ties by index, the host planner's
@@ -29,6 +30,11 @@ namespace {
 constexpr int kPlanThreads = 256;
 static_assert(kPlanThreads >= kMaxBatch, "one thread per request");
 
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 struct PlanParams {
   int32_t batch, q_len, heads, rows, tiles, nt;
   int32_t max_kv_len, split_kv, max_split_kv, num_cus, cap_parts, max_groups;
@@ -44,6 +50,8 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
   __shared__ int32_t s_order[kMaxBatch];
   __shared__ int32_t s_max;
   __shared__ long long s_waves[5];  // sum_b rows min(16 >> k, S_b), k = 0..4
+  __shared__ int32_t s_maxp;
+  __shared__ int32_t s_part[kPlanThreads / 64];
   const int b = threadIdx.x;
   const bool live = b < pp.batch;
 
@@ -51,22 +59,46 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
   if (live) L = min(max(kv_lens[b], 0), pp.max_kv_len);
   const int64_t pages = ((int64_t)L + kPage - 1) / kPage;
   red[b] = live ? pages : 0;
+  if (b == 0) s_maxp = 1;
   __syncthreads();
+  if (live) atomicMax(&s_maxp, (int32_t)pages);  // LDS atomic
   for (int w = kPlanThreads / 2; w > 0; w >>= 1) {
     if (b < w) red[b] += red[b + w];
     __syncthreads();
   }
   const int64_t total_pages = red[0];
 
+  // proportional plan: the smallest split length C (pages) with
+  // sum_b clamp(ceil(pages_b / C), 1, cap) <= budget; every thread runs the same search
+  int64_t C = 1;
+  if (pp.split_kv <= 0) {
+    const int64_t Bn = pp.batch, budget = pp.budget;
+    int64_t lo = 1, hi = max((int64_t)1, (int64_t)s_maxp);
+    if (budget > Bn) hi = min(hi, (total_pages + (budget - Bn) - 1) / (budget - Bn));
+    else lo = hi;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      int32_t n = live ? (int32_t)min(max((pages + mid - 1) / mid, (int64_t)1),
+                                      (int64_t)pp.max_split_kv)
+                       : 0;
+      n = wave_sum(n);
+      if ((b & 63) == 0) s_part[b >> 6] = n;
+      __syncthreads();
+      int64_t tot = 0;
+#pragma unroll
+      for (int w = 0; w < kPlanThreads / 64; ++w) tot += s_part[w];
+      __syncthreads();
+      if (tot <= budget) hi = mid; else lo = mid + 1;
+    }
+    C = lo;
+  }
+
   if (live) {
     int64_t want;
     if (pp.split_kv > 0) {
       want = min(pp.split_kv, pp.max_split_kv);
     } else {
-      const double per_page = total_pages > 0
-          ? (double)pp.budget / (double)total_pages : 0.0;
-      want = (int64_t)(per_page * (double)pages);
-      want = max((int64_t)1, min(want, (int64_t)pp.max_split_kv));
+      want = max((int64_t)1, min((pages + C - 1) / C, (int64_t)pp.max_split_kv));
     }
     int64_t s = max((int64_t)1, min(want, max(pages, (int64_t)1)));
     s = max(s, (pages + kMaxChunkPages - 1) / kMaxChunkPages);
