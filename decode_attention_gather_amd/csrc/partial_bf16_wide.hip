@@ -273,7 +273,9 @@ __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
           if (kMasked && tok0 + jj >= lim_q[k]) v = -INFINITY;
           t[k][tt][jj] = v;
         }
-        c[k][tt] = fmaxf(fmaxf(t[k][tt][0], t[k][tt][1]), fmaxf(t[k][tt][2], t[k][tt][3]));
+        c[k][tt] = __builtin_elementwise_maximum(  // IEEE maximum: no quieting
+            __builtin_elementwise_maximum(t[k][tt][0], t[k][tt][1]),
+            __builtin_elementwise_maximum(t[k][tt][2], t[k][tt][3]));
       } else if (slice == 1) {
         c[k][tt] = ceilf(group_max4(c[k][tt]));  // -inf when no key of the tile is visible
       } else if (slice == 2) {

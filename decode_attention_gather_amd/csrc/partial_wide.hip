@@ -306,8 +306,12 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
             for (int jj = 0; jj < 4; ++jj)
               if (tok_page + 16 * tt + 4 * g + jj >= lim_q[k]) t[tt][jj] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(t[0][0], t[0][1]), fmaxf(t[0][2], t[0][3])),
-                         fmaxf(fmaxf(t[1][0], t[1][1]), fmaxf(t[1][2], t[1][3])));
+        // IEEE maximum: no quieting of the values that come through the mask branch
+        float mx = __builtin_elementwise_maximum(
+            __builtin_elementwise_maximum(__builtin_elementwise_maximum(t[0][0], t[0][1]),
+                                          __builtin_elementwise_maximum(t[0][2], t[0][3])),
+            __builtin_elementwise_maximum(__builtin_elementwise_maximum(t[1][0], t[1][1]),
+                                          __builtin_elementwise_maximum(t[1][2], t[1][3])));
         mx = group_max4(mx);
         const float c = ceilf(mx);  // -inf when no key of the page is visible to the row
         const float off = 8.f - (c == -INFINITY ? 0.f : c);
