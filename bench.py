@@ -96,6 +96,27 @@ def profiled_traffic(config: str, kernel: str = "partial_kernel", source: str = 
     return int(fields["traffic_bytes_per_launch"])
 
 
+def roofline(name: str, case, by: dict, partial_us: float) -> dict:
+    """The `roofline` object for the partial kernel of a workload: MFMA-bound when its
+    algorithmic flops per algorithmic byte exceed the ridge (dense MFMA peak / 8 TB/s),
+    else HBM-bound; achieved = algorithmic flops or bytes per launch / launch time."""
+    kname, ksrc = dominant_kernel(case.kv_dtype, case.q_len * case.num_heads)
+    flops = algorithmic_flops(case.kv_lens.tolist(), case.q_len, case.num_heads)
+    peak_tf = mfma_peak(case.kv_dtype)  # TFLOP/s
+    if flops / by["partial_in"] > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / (partial_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
+                "peak": peak_tf, "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4),
+                "flops_per_launch": flops}
+    else:
+        achieved = by["partial_in"] / (partial_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": profiled_traffic(name, kname, ksrc),
+                 "bytes_per_launch": by["partial_in"], "us_per_launch": partial_us})
+    return roof
+
+
 def time_steps(fn, steps, warmup, stream):
     """`warmup` untimed calls, then exactly `steps` back-to-back calls bracketed by
     torch.cuda.synchronize(), timed by one HIP event pair on `stream` (nothing else is
@@ -386,22 +407,7 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(case)
 
-    kname, ksrc = dominant_kernel(case.kv_dtype, case.q_len * case.num_heads)
-    # the partial kernel's bound: MFMA when its algorithmic flops per algorithmic byte
-    # exceed the ridge (dense MFMA peak / 8 TB/s), else HBM
-    flops = algorithmic_flops(case.kv_lens.tolist(), case.q_len, case.num_heads)
-    peak_tf = mfma_peak(case.kv_dtype)  # TFLOP/s
-    if flops / by["partial_in"] > peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
-        achieved = flops / (native["partial_us"] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 2),
-                "peak": peak_tf, "unit": "TFLOP/s", "frac": round(achieved / peak_tf, 4),
-                "flops_per_launch": flops}
-    else:
-        achieved = by["partial_in"] / (native["partial_us"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": profiled_traffic(name, kname, ksrc),
-                 "bytes_per_launch": by["partial_in"], "us_per_launch": native["partial_us"]})
+    roof = roofline(name, case, by, native["partial_us"])
     res = {
         "metric": METRIC,
         "value": native["kv_gbs"],
