@@ -280,11 +280,19 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   plan->split_kv = split_kv;
   plan->max_split_kv = max_split_kv;
   plan->kv_lens = nullptr;
-  // launch width: the widest merge any lengths can ask for (the device planner applies
-  // the budget to the actual splits and picks <= this)
-  // slices as for a batch of equal requests at the largest split count
+  // merge slices as for a batch of equal requests at the largest split count
   plan->merge_slices = merge_slices_for(std::vector<int64_t>(batch, per_req), rows, num_cus);
-  plan->merge_groups = merge_groups_for(std::vector<int64_t>(1, per_req), 0, num_cus);
+  // launch width: at most min(16, largest split count), halved while the launch would
+  // start more than 64 waves per CU (B rows G); the device planner applies the host rule
+  // to the actual splits and picks <= this, so graph and host plans of the same lengths
+  // merge alike whenever the host's width fits under it. A launch at the unhalved width
+  // starts 16 waves per row even where one folds everything (6144 rows: 39 us of merge).
+  {
+    int32_t g = 1;
+    while (g * 2 <= 16 && g * 2 <= per_req) g *= 2;
+    while (g > 1 && (int64_t)batch * rows * g > 2LL * kMergeWavesPerCu * num_cus) g /= 2;
+    plan->merge_groups = g;
+  }
   d.groups = plan->merge_groups;
   plan->max_splits = (int32_t)per_req;
   plan->num_cus = num_cus;

@@ -34,6 +34,15 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+__device__ __forceinline__ long long wave_sum64(long long v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+constexpr int kPlanWaves = kPlanThreads / 64;
 
 struct PlanParams {
   int32_t batch, q_len, heads, rows, tiles, nt;
@@ -44,49 +53,57 @@ struct PlanParams {
 __global__ void __launch_bounds__(kPlanThreads)
 device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
                    PlanDev* __restrict__ out) {
-  __shared__ int64_t red[kPlanThreads];
   __shared__ int32_t s_splits[kMaxBatch];
   __shared__ int32_t s_chunk[kMaxBatch];
   __shared__ int32_t s_order[kMaxBatch];
-  __shared__ int32_t s_max;
-  __shared__ long long s_waves[5];  // sum_b rows min(16 >> k, S_b), k = 0..4
-  __shared__ int32_t s_maxp;
-  __shared__ int32_t s_part[kPlanThreads / 64];
+  // per-wave partial results (wave reductions, then one pass over the 4 waves: no
+  // contended LDS atomics)
+  __shared__ int32_t s_part[kPlanWaves];
+  __shared__ int32_t s_pmax[kPlanWaves];
+  __shared__ long long s_psum[kPlanWaves];
+  __shared__ int32_t s_smax[kPlanWaves];
+  __shared__ int32_t s_wpart[5][kPlanWaves];  // sum_b rows min(16 >> k, S_b), k = 0..4
   const int b = threadIdx.x;
   const bool live = b < pp.batch;
 
   int32_t L = 0;
   if (live) L = min(max(kv_lens[b], 0), pp.max_kv_len);
   const int64_t pages = ((int64_t)L + kPage - 1) / kPage;
-  red[b] = live ? pages : 0;
-  if (b == 0) s_maxp = 1;
-  __syncthreads();
-  if (live) atomicMax(&s_maxp, (int32_t)pages);  // LDS atomic
-  for (int w = kPlanThreads / 2; w > 0; w >>= 1) {
-    if (b < w) red[b] += red[b + w];
-    __syncthreads();
+  {
+    const int32_t pm = wave_max(live ? (int32_t)pages : 1);   // pages <= 2^26
+    const long long ps = wave_sum64(live ? pages : 0);        // up to 64 x 2^26
+    if ((b & 63) == 0) {
+      s_pmax[b >> 6] = pm;
+      s_psum[b >> 6] = ps;
+    }
   }
-  const int64_t total_pages = red[0];
+  __syncthreads();
+  int64_t total_pages = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) total_pages += s_psum[w];
 
   // proportional plan: the smallest split length C (pages) with
   // sum_b clamp(ceil(pages_b / C), 1, cap) <= budget; every thread runs the same search
   int64_t C = 1;
   if (pp.split_kv <= 0) {
     const int64_t Bn = pp.batch, budget = pp.budget;
-    int64_t lo = 1, hi = max((int64_t)1, (int64_t)s_maxp);
+    int32_t maxp = 1;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) maxp = max(maxp, s_pmax[w]);
+    int64_t lo = 1, hi = maxp;
     if (budget > Bn) hi = min(hi, (total_pages + (budget - Bn) - 1) / (budget - Bn));
     else lo = hi;
     while (lo < hi) {
-      const int64_t mid = lo + (hi - lo) / 2;
-      int32_t n = live ? (int32_t)min(max((pages + mid - 1) / mid, (int64_t)1),
-                                      (int64_t)pp.max_split_kv)
+      const int64_t mid = lo + (hi - lo) / 2;  // <= max pages < 2^27: 32-bit division
+      const uint32_t p32 = (uint32_t)pages, m32 = (uint32_t)mid;
+      int32_t n = live ? (int32_t)min(max((p32 + m32 - 1u) / m32, 1u), (uint32_t)pp.max_split_kv)
                        : 0;
       n = wave_sum(n);
       if ((b & 63) == 0) s_part[b >> 6] = n;
       __syncthreads();
       int64_t tot = 0;
 #pragma unroll
-      for (int w = 0; w < kPlanThreads / 64; ++w) tot += s_part[w];
+      for (int w = 0; w < kPlanWaves; ++w) tot += s_part[w];
       __syncthreads();
       if (tot <= budget) hi = mid; else lo = mid + 1;
     }
@@ -100,25 +117,30 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
     } else {
       want = max((int64_t)1, min((pages + C - 1) / C, (int64_t)pp.max_split_kv));
     }
-    int64_t s = max((int64_t)1, min(want, max(pages, (int64_t)1)));
-    s = max(s, (pages + kMaxChunkPages - 1) / kMaxChunkPages);
-    const int64_t chunk = max((int64_t)1, (pages + s - 1) / s);
-    s = max((int64_t)1, (pages + chunk - 1) / chunk);
+    // pages < 2^27 and s <= pages: 32-bit divisions
+    const uint32_t p32 = (uint32_t)pages;
+    uint32_t s = (uint32_t)max((int64_t)1, min(want, max(pages, (int64_t)1)));
+    s = max(s, (p32 + kMaxChunkPages - 1u) / kMaxChunkPages);
+    const uint32_t chunk = max(1u, (p32 + s - 1u) / s);
+    s = max(1u, (p32 + chunk - 1u) / chunk);
     s_splits[b] = (int32_t)s;
     s_chunk[b] = (int32_t)chunk;
     out->kv_len[b] = (uint32_t)L;
     out->splits[b] = (uint16_t)s;
   }
-  if (b == 0) s_max = 0;
-  if (b < 5) s_waves[b] = 0;
-  __syncthreads();
-  if (live) {
-    atomicMax(&s_max, s_splits[b]);  // LDS atomics
+  {
+    const int32_t sb = live ? s_splits[b] : 0;
+    const int32_t sm = wave_max(sb);
+    int32_t wv[5];
 #pragma unroll
-    for (int k = 0; k < 5; ++k)
-      atomicAdd((unsigned long long*)&s_waves[k],
-                (unsigned long long)pp.rows * (unsigned long long)min(16 >> k, s_splits[b]));
+    for (int k = 0; k < 5; ++k) wv[k] = wave_sum(pp.rows * min(16 >> k, sb));  // <= 2^22 each
+    if ((b & 63) == 0) {
+      s_smax[b >> 6] = sm;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) s_wpart[k][b >> 6] = wv[k];
+    }
   }
+  __syncthreads();
   if (live) {
     int32_t base = 0, rank = 0;
     for (int i = 0; i < pp.batch; ++i) {
@@ -144,6 +166,14 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       out->total_parts = (int32_t)min(run, (uint32_t)pp.cap_parts);
       out->nt = pp.nt;
       // merge width by the host planner's rule, from the actual splits
+      int32_t s_max = 0;
+      long long s_waves[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < kPlanWaves; ++w) {
+        s_max = max(s_max, s_smax[w]);
+#pragma unroll
+        for (int k = 0; k < 5; ++k) s_waves[k] += s_wpart[k][w];
+      }
       int32_t g = 1;
       while (g * 2 <= 16 && g * 2 <= s_max) g *= 2;
       auto waves = [&](int32_t gg) { return s_waves[__builtin_ctz(16 / gg)]; };
