@@ -65,9 +65,10 @@ constexpr int kOnesE4M3 = 0x38383838;                 // four E4M3 1.0
 
 // Wave roles. Every wave is one of: QK (one page of the step for one row tile: wave
 // w < 2 NT takes page w & 1 and row tile w >> 1), loader (36 / kLdWaves chunks of 1 KB
-// per step), PV (kDimTiles of the 32 16-dim tiles of O for all NT row tiles).
-//  NT = 1: 12 waves (3 per SIMD, 168 VGPRs): 2 QK, 6 loaders, 4 PV x 8 dim tiles.
-//  NT = 2: 16 waves (4 per SIMD, 128 VGPRs): 4 QK, 4 loaders, 8 PV x 4 dim tiles.
+// per step), PV (8 of the 32 16-dim tiles of O for one row tile; four PV waves per row
+// tile, so a PV wave holds the same state whatever NT is).
+//  NT = 1: 12 waves (3 per SIMD, 168 VGPRs): 2 QK, 6 loaders, 4 PV.
+//  NT = 2: 16 waves (4 per SIMD, 128 VGPRs): 4 QK, 4 loaders, 8 PV.
 template <int NT>
 struct Roles {
   static_assert(NT == 1 || NT == 2, "row tiles per workgroup");
@@ -77,7 +78,9 @@ struct Roles {
   static constexpr int kLdFirst = 2 * NT;
   static constexpr int kLdWaves = NT == 1 ? 6 : 4;
   static constexpr int kPVFirst = kLdFirst + kLdWaves;
-  static constexpr int kDimTiles = 32 / (kWaves - kPVFirst);  // 8 or 4
+  static constexpr int kDimTiles = 32 * NT / (kWaves - kPVFirst);  // 8: dim tiles per PV wave
+  static constexpr int kDimSlices = 32 / kDimTiles;                // 4 PV waves per row tile
+  static_assert(kDimSlices * NT == kWaves - kPVFirst, "PV waves cover every (row tile, dim slice)");
   static constexpr int kMaxLd = kChunksPerStep / kLdWaves;    // 6 or 9
 };
 
@@ -284,14 +287,17 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   };
 
   // ---------------- PV role ----------------
-  const int pv_w = w - R::kPVFirst;  // dims [16 kDimTiles pv_w, ...)
+  const int pv_w = w - R::kPVFirst;
+  const int pv_rt = pv_w / R::kDimSlices;  // row tile of the wave
+  const int pv_ds = pv_w % R::kDimSlices;  // dims [16 kDimTiles pv_ds, ...)
+  const bool pv_own = pv_ds == 0;          // the wave that keeps l and l~ of its row tile
   constexpr int kDT = kDoPV ? R::kDimTiles : 1;
-  constexpr int kNTp = kDoPV ? NT : 1;
+  constexpr int kNTp = 1;                  // row tiles per PV wave (rt below is 0)
   v4f acc[kNTp][kDT];
-  v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile pv_w (pv_w < NT): ones product
+  v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile pv_rt (pv_own): ones product
   float m_c[kNTp][4];  // running max of result rows
-  float m_a[kNTp];     // running max of operand rows (row l16 of each tile)
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // l of rows 4g + jj of row tile pv_w
+  float m_a[kNTp];     // running max of operand rows (row l16 of the tile)
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // l of rows 4g + jj of row tile pv_rt (pv_own)
 #pragma unroll
   for (int rt = 0; rt < kNTp; ++rt) {
     m_a[rt] = -INFINITY;
@@ -307,7 +313,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   for (int r = 0; r < 2; ++r) {
     const int tokstep = 16 * g + 8 * r + (l16 >> 1);
     const int pg = tokstep >> 5, n = tokstep & 31;
-    tr_base[r] = pg * kPageLds + n * kRowLds + 8 * (l16 & 1) + 16 * R::kDimTiles * pv_w;
+    tr_base[r] = pg * kPageLds + n * kRowLds + 8 * (l16 & 1) + 16 * R::kDimTiles * pv_ds;
   }
 
   auto pv_step = [&](int st) {
@@ -321,12 +327,12 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
       float alpha[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float2 p0 = sm.cl[pb][rt * kTileRows + 4 * g + jj][0];
-        const float2 p1 = sm.cl[pb][rt * kTileRows + 4 * g + jj][1];
+        const float2 p0 = sm.cl[pb][(pv_rt + rt) * kTileRows + 4 * g + jj][0];
+        const float2 p1 = sm.cl[pb][(pv_rt + rt) * kTileRows + 4 * g + jj][1];
         const float mn = fmaxf(m_c[rt][jj], fmaxf(p0.x, p1.x));
         alpha[jj] = mn == m_c[rt][jj] ? 1.f : pow2_diff(m_c[rt][jj], mn);
         rescale |= mn != m_c[rt][jj];
-        if (rt == pv_w)
+        if (pv_own)
           lsum[jj] = lsum[jj] * alpha[jj] + p0.y * pow2_diff(p0.x, mn) + p1.y * pow2_diff(p1.x, mn);
         m_c[rt][jj] = mn;
       }
@@ -336,18 +342,18 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
           acc[rt][d][0] *= alpha[0]; acc[rt][d][1] *= alpha[1];
           acc[rt][d][2] *= alpha[2]; acc[rt][d][3] *= alpha[3];
         }
-        if (rt == pv_w) {
+        if (pv_own) {
           acc1[0] *= alpha[0]; acc1[1] *= alpha[1]; acc1[2] *= alpha[2]; acc1[3] *= alpha[3];
         }
       }
-      const float2 a0 = sm.cl[pb][rt * kTileRows + l16][0];
-      const float2 a1 = sm.cl[pb][rt * kTileRows + l16][1];
+      const float2 a0 = sm.cl[pb][(pv_rt + rt) * kTileRows + l16][0];
+      const float2 a1 = sm.cl[pb][(pv_rt + rt) * kTileRows + l16][1];
       m_a[rt] = fmaxf(m_a[rt], fmaxf(a0.x, a1.x));
       const float cp = (g & 1) ? a1.x : a0.x;
       sa[rt] = cp == -INFINITY ? 127 : max(0, 127 + (int)(cp - m_a[rt]) - 4 * (g >> 1));
-      const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 16 * g;
+      const uint8_t* prow = sm.ptile[pb] + ((pv_rt + rt) * kTileRows + l16) * kPRow + 16 * g;
       pa[rt] = cat8(ld16(prow, 0), ld16(prow, 64));
-      if (rt == pv_w) {
+      if (pv_own) {
         const v8i ones = v8i{kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
                              kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
         acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[rt], ones, acc1, 0, 0, 0, sa[rt], 0, 127);
@@ -434,12 +440,12 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
     for (int rt = 0; rt < kNTp; ++rt) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int row = row0 + rt * kTileRows + 4 * g + jj;
+        const int row = row0 + (pv_rt + rt) * kTileRows + 4 * g + jj;
         if (row < P.rows) {
-          float* orow = it.ws_o + (part_row0 + row) * kDV + 16 * R::kDimTiles * pv_w + l16;
+          float* orow = it.ws_o + (part_row0 + row) * kDV + 16 * R::kDimTiles * pv_ds + l16;
 #pragma unroll
           for (int d = 0; d < kDT; ++d) orow[16 * d] = acc[rt][d][jj];
-          if (rt == pv_w && l16 == 0)
+          if (pv_own && l16 == 0)
             *(float4*)(it.ws_stats + (part_row0 + row) * kStatStride) =
                 make_float4(m_c[rt][jj], lsum[jj], acc1[jj], 0.f);
         }
