@@ -127,7 +127,8 @@ __device__ __forceinline__ void block_sync_lds() {
 // One wave-wide direct-to-LDS load (lane i's 16 bytes at sbase + voff land at LDS byte
 // lds_base + 16 i), from inline asm so that the compiler's wait counts do not drain it
 // at every LDS access; M0 carries the LDS base and is restored; the s_nop covers the
-// wait states after a VALU write of an SGPR the load reads.
+// wait states after a VALU write of an SGPR the load reads; nt marks the read-once
+// stream of cache pages non-temporal.
 __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
   uint32_t saved;
@@ -135,7 +136,7 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(base)

@@ -112,7 +112,9 @@ __device__ __forceinline__ void block_sync_lds() {
 // wait-count pass does not drain it at every LDS access; M0 carries the LDS base and is
 // restored. The s_nop covers the wait states a vector memory instruction needs after a
 // VALU write of an SGPR it reads (the base may come from v_readfirstlane), which the
-// compiler does not insert in front of inline assembly.
+// compiler does not insert in front of inline assembly. The nt (non-temporal) policy
+// marks the stream of cache pages as read-once, as the narrow kernels' loads are
+// (measured: 1-2% faster on the q = 8 shapes, bit-identical).
 __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
   uint32_t saved;
@@ -120,7 +122,7 @@ __device__ __forceinline__ void dma16(uint64_t sbase, uint32_t voff, uint32_t ld
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(base)
