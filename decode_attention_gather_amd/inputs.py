@@ -169,6 +169,10 @@ CONFIGS = {
                                 seed=20268, kv_dtype="bf16"),
     "b_b16_h12_q1_128k_bf16": dict(kv_lens=[131072] * 16, num_heads=12, q_len=1, split_kv=6,
                                    seed=20269, kv_dtype="bf16"),
+    # 32 rows per request (16 heads, 2 causal query tokens): the two-row-tile narrow kernel
+    # at the headline's KV size
+    "t_b16_h16_q2_128k": dict(kv_lens=[131072] * 16, num_heads=16, q_len=2, split_kv=0,
+                              seed=20270),
 }
 
 

@@ -240,7 +240,7 @@ def test_merge_synthetic(mla, lens, split, heads, q_len):
 # ---- full-size workloads (launch configuration of the benchmark), sampled rows --------
 
 FULL = ["c1_b1_h12_q1_2k", "c2_b4_h12_q1_128k", "c3_b16_h12_q8_128k", "c4_b1_h12_q1_1m",
-        "c5_b8_h96_q8_mixed", "m_b16_h12_q1_128k", "s_b8_h12_q8_skewed"]
+        "c5_b8_h96_q8_mixed", "m_b16_h12_q1_128k", "s_b8_h12_q8_skewed", "t_b16_h16_q2_128k"]
 
 
 @pytest.mark.parametrize("name", FULL)
