@@ -298,15 +298,35 @@ def cpu_baseline(case, budget_rows=None):
                       output_scale=case.output_scale, rows=rows, nthreads=threads,
                       kv_dtype=case.kv_dtype)
     dt = time.perf_counter() - t0
-    call_s = dt * case.rows / len(rows)
+    # scale by visible row-tokens (the oracle's work), not rows: lengths may differ
+    per_req = case.q_len * case.num_heads
+    lens = case.kv_lens.tolist()
+
+    def vis(r):
+        L = int(lens[r // per_req])
+        return L - case.q_len + (r % per_req) // case.num_heads + 1
+
+    total = sum(vis(r) for r in range(case.rows))
+    call_s = dt * total / max(sum(vis(r) for r in rows), 1)
     return dict(value=round(case.kv_bytes / call_s / 1e9, 4), unit="GB/s", cores=threads,
                 kind="oracle", us_per_call=round(call_s * 1e6, 1),
                 sample=f"{len(rows)} of {case.rows} rows (every KV token of each), "
-                       f"{dt:.2f} s on {threads} threads, scaled to the full call")
+                       f"{dt:.2f} s on {threads} threads, scaled to the full call by "
+                       "visible row-tokens")
 
 
-def bench_other(mla, name, steps, warmup):
-    """Every plan of one more workload (stderr report and the JSON's `all` list)."""
+# row-tokens of fp64 oracle work per workload in `--all` (about 2 s on 16 host threads)
+ORACLE_ROW_TOKENS = 50_000_000
+
+
+def oracle_rows(case) -> int:
+    """Rows of a bounded oracle sample: about ORACLE_ROW_TOKENS row-tokens, at least 16."""
+    return min(case.rows, max(16, ORACLE_ROW_TOKENS // int(max(case.kv_lens.max(), 1))))
+
+
+def bench_other(mla, name, steps, warmup, cpu=False):
+    """Every plan of one more workload (stderr report and the JSON's `all` list); with
+    `cpu`, the oracle on a bounded sample of its rows is attached to the last plan."""
     c = inputs.make_config(name)
     dc = mla.to_device(c)
     by = algorithmic_bytes(c)
@@ -322,6 +342,8 @@ def bench_other(mla, name, steps, warmup):
         out[-1]["graph"] = graph_timing(mla, dc, c)
     if name.startswith("s_"):
         out[-1]["graph_path"] = graph_path(mla, dc, dc.q, c.rows, by["kv"], steps, warmup)
+    if cpu:
+        out[-1]["cpu_baseline"] = cpu_baseline(c, oracle_rows(c))
     del dc
     torch.cuda.empty_cache()
     return out
@@ -401,7 +423,7 @@ def main():
         for other in sorted(inputs.CONFIGS):
             if other == name:
                 continue
-            for r in bench_other(mla, other, steps, warmup):
+            for r in bench_other(mla, other, steps, warmup, cpu=not args.no_cpu):
                 print("[bench-all] " + json.dumps(r), file=sys.stderr, flush=True)
                 others.append(r)
 

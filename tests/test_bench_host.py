@@ -83,3 +83,17 @@ def test_traffic_only_while_the_source_hash_matches(tmp_path, monkeypatch):
     (csrc / "k.hip").write_bytes(b"kernel source, edited")
     assert bench.profiled_traffic("w", "k_kernel", "k.hip") is None
     assert bench.profiled_traffic("other", "k_kernel", "k.hip") is None
+
+
+@pytest.mark.parametrize("lens, q, h", [
+    ([2048], 1, 12),            # small: every row
+    ([1048576], 1, 12),         # one long request: every row, 12 x 1M row-tokens
+    ([131072] * 16, 8, 12),     # 1536 rows: a sample within the row-token budget
+    ([1048576] + [4096] * 7, 8, 12),
+])
+def test_oracle_sample_is_bounded(lens, q, h):
+    case = fake_case(lens, q, h, "e4m3")
+    n = bench.oracle_rows(case)
+    assert 1 <= n <= case.rows
+    assert n == case.rows or n == 16 or n * max(lens) <= bench.ORACLE_ROW_TOKENS
+    assert n >= min(16, case.rows)
