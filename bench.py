@@ -286,10 +286,11 @@ def graph_timing(mla, dc, case, calls=100, reps=5):
                 floor_us_per_2_kernels=round(floor, 2), graph_matches_eager=same)
 
 
-def cpu_baseline(case, budget_rows=None):
-    """The fp64 oracle on a bounded sample of the workload's rows (all host cores)."""
+def cpu_baseline(case, budget_rows=None, threads=None):
+    """The fp64 oracle on a bounded sample of the workload's rows (all host cores, or
+    `threads` of them)."""
     import oracle
-    threads = oracle.hw_threads()
+    threads = threads or oracle.hw_threads()
     nrows = min(budget_rows or case.rows, case.rows)
     rows = inputs.sample_rows(case, nrows)
     t0 = time.perf_counter()
@@ -319,9 +320,9 @@ def cpu_baseline(case, budget_rows=None):
 ORACLE_ROW_TOKENS = 50_000_000
 
 
-def oracle_rows(case) -> int:
-    """Rows of a bounded oracle sample: about ORACLE_ROW_TOKENS row-tokens, at least 16."""
-    return min(case.rows, max(16, ORACLE_ROW_TOKENS // int(max(case.kv_lens.max(), 1))))
+def oracle_rows(case, row_tokens: int = ORACLE_ROW_TOKENS) -> int:
+    """Rows of a bounded oracle sample: about `row_tokens` row-tokens, at least 16."""
+    return min(case.rows, max(16, row_tokens // int(max(case.kv_lens.max(), 1))))
 
 
 def bench_other(mla, name, steps, warmup, cpu=False):
@@ -344,6 +345,9 @@ def bench_other(mla, name, steps, warmup, cpu=False):
         out[-1]["graph_path"] = graph_path(mla, dc, dc.q, c.rows, by["kv"], steps, warmup)
     if cpu:
         out[-1]["cpu_baseline"] = cpu_baseline(c, oracle_rows(c))
+        # one host thread: the whole call for the small workload, else a smaller sample
+        out[-1]["cpu_baseline_1thread"] = cpu_baseline(
+            c, oracle_rows(c, ORACLE_ROW_TOKENS // 16), threads=1)
     del dc
     torch.cuda.empty_cache()
     return out
