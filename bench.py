@@ -223,10 +223,41 @@ def graph_path(mla, dc, q, rows, kv_bytes, steps, warmup):
         mla.decode_graph(plan, q, dc.kv, dc.block_table, dc.kv_lens, ss, os_, ws, o, lse, stream)
 
     us, per, _ = time_steps(call, steps, warmup, stream)
+    replayed = graph_replay(mla, plan, q, dc, ss, os_, ws, o, lse, kv_bytes)
     info = plan.info()[0]
     plan.close()
     return dict(us_per_call=round(us, 2), call=stats(per), work_item_capacity=info.work_items,
-                kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1))
+                kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1), replayed=replayed)
+
+
+def graph_replay(mla, plan, q, dc, ss, os_, ws, o, lse, kv_bytes, calls=20, reps=5):
+    """The graph-path call as it is meant to run: `calls` of them captured in one HIP
+    graph and replayed (median over `reps` replays), checked against the eager output."""
+    torch.cuda.synchronize()
+    o_eager, lse_eager = o.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                mla.decode_graph(plan, q, dc.kv, dc.block_table, dc.kv_lens, ss, os_, ws, o, lse, s)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / calls)
+    us = float(np.median(per))
+    same = bool(torch.equal(o, o_eager) and torch.equal(lse, lse_eager))
+    return dict(calls_per_graph=calls, us_per_call=round(us, 2),
+                kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1), matches_eager=same)
 
 
 def q8_sibling(case, q_len=8, seed=20263):
