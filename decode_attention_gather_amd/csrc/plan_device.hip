@@ -30,19 +30,48 @@ namespace {
 constexpr int kPlanThreads = 256;
 static_assert(kPlanThreads >= kMaxBatch, "one thread per request");
 
+// Sum over the 64 lanes, every lane receiving it: row rotations by 8, 4, 2, 1 (DPP)
+// sum each 16-lane row, then the VALU lane swaps add lanes l ^ 32 and l ^ 16. No LDS
+// round trip, unlike a shuffle chain: this sum sits on the planner's critical path, once
+// per step of its binary search. All 64 lanes must be active.
 __device__ __forceinline__ int32_t wave_sum(int32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x122, 0xF, 0xF, false);  // row_ror:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x121, 0xF, 0xF, false);  // row_ror:1
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = (int32_t)(a[0] + a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (int32_t)(b[0] + b[1]);
 }
 __device__ __forceinline__ long long wave_sum64(long long v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ int32_t wave_max(int32_t v) {
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+__device__ __forceinline__ int32_t wave_max(int32_t v) {  // as wave_sum, with max
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x122, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x121, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((int32_t)a[0], (int32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((int32_t)b[0], (int32_t)b[1]);
 }
 constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Inclusive prefix sum over the 64 lanes (lane l receives the sum of lanes 0..l): row
+// shifts by 1, 2, 4, 8 within each 16-lane row, then the last lane of row 0 added to
+// rows 1-3 and that of row 1 to rows 2-3 (DPP row broadcasts). All lanes must be active.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
 
 struct PlanParams {
   int32_t batch, q_len, heads, rows, tiles, nt;
@@ -93,18 +122,33 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
     int64_t lo = 1, hi = maxp;
     if (budget > Bn) hi = min(hi, (total_pages + (budget - Bn) - 1) / (budget - Bn));
     else lo = hi;
+    // Up to 64 requests, every wave holds all of them (lane = request) and runs the
+    // search on its own, with no barrier per step; beyond that the waves' sums meet in
+    // LDS. Both orders of summation are exact (integers), so the plan is the same.
+    const bool one_wave = pp.batch <= 64;
+    const int lane = b & 63;
+    uint32_t ps32 = (uint32_t)pages;
+    bool s_live = live;
+    if (one_wave) {
+      s_live = lane < pp.batch;
+      const int32_t Ll = s_live ? min(max(kv_lens[lane], 0), pp.max_kv_len) : 0;
+      ps32 = (uint32_t)(((int64_t)Ll + kPage - 1) / kPage);
+    }
     while (lo < hi) {
       const int64_t mid = lo + (hi - lo) / 2;  // <= max pages < 2^27: 32-bit division
-      const uint32_t p32 = (uint32_t)pages, m32 = (uint32_t)mid;
-      int32_t n = live ? (int32_t)min(max((p32 + m32 - 1u) / m32, 1u), (uint32_t)pp.max_split_kv)
-                       : 0;
+      const uint32_t m32 = (uint32_t)mid;
+      int32_t n = s_live ? (int32_t)min(max((ps32 + m32 - 1u) / m32, 1u), (uint32_t)pp.max_split_kv)
+                         : 0;
       n = wave_sum(n);
-      if ((b & 63) == 0) s_part[b >> 6] = n;
-      __syncthreads();
-      int64_t tot = 0;
+      int64_t tot = n;
+      if (!one_wave) {
+        if ((b & 63) == 0) s_part[b >> 6] = n;
+        __syncthreads();
+        tot = 0;
 #pragma unroll
-      for (int w = 0; w < kPlanWaves; ++w) tot += s_part[w];
-      __syncthreads();
+        for (int w = 0; w < kPlanWaves; ++w) tot += s_part[w];
+        __syncthreads();
+      }
       if (tot <= budget) hi = mid; else lo = mid + 1;
     }
     C = lo;
@@ -151,9 +195,15 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
     s_order[rank] = b;
   }
   __syncthreads();
-  if (live) {
-    uint32_t run = 0;
+  // running split count along the issue order: one wave-wide inclusive scan when the
+  // batch fits in wave 0, else a walk over the order
+  uint32_t run = 0;
+  if (pp.batch <= 64) {
+    if (b < 64) run = wave_scan((uint32_t)(live ? s_splits[s_order[b]] : 0));
+  } else if (live) {
     for (int e = 0; e <= b; ++e) run += (uint32_t)s_splits[s_order[e]];
+  }
+  if (live) {
     out->sorted[b] = (run << 8) | (uint32_t)s_order[b];
     if (b == pp.batch - 1) {
       out->batch = pp.batch;

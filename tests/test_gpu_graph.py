@@ -149,3 +149,27 @@ def test_graph_capture_replay(mla):
         assert_parity(o_g.float().cpu().numpy(), lse_g.cpu().numpy(), o_ref, lse_ref,
                       f"replay {i}")
         assert torch.equal(o_g, o_e) and torch.equal(lse_g, lse_e), f"replay {i} != eager"
+
+
+# The device planner searches one wave per request set up to 64 requests and across
+# waves beyond: both sides of that line, against the host planner, bit for bit.
+@pytest.mark.parametrize("batch", [63, 64, 65, 100, 256])
+def test_graph_equals_host_across_batch_sizes(mla, batch):
+    g = torch.Generator().manual_seed(9000 + batch)
+    lens = torch.randint(33, 1500, (batch,), generator=g).tolist()
+    _say(f"[gpu] graph vs host: batch={batch} lens {min(lens)}..{max(lens)}")
+    case = inputs.make_case(lens, num_heads=12, q_len=1, seed=900 + batch, split_kv=0)
+    dc = mla.to_device(case)
+    plan = mla.Plan.graph(batch, q_len=1, num_heads=12, max_kv_len=max(lens))
+    ws = plan.alloc_workspace()
+    o, lse = graph_call(mla, plan, dc, dc.kv_lens, scal(case.softmax_scale),
+                        scal(case.output_scale), ws)
+    hplan = mla.Plan(lens, q_len=1, num_heads=12, split_kv=0)
+    o_h, lse_h = mla.run_decode(dc, hplan)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_h), "graph path differs from host plan"
+    assert torch.equal(lse, lse_h)
+    rows = inputs.sample_rows(case, 8)
+    o_ref, lse_ref = run_oracle(case, rows)
+    assert_parity(o.float().cpu().numpy()[rows], lse.cpu().numpy()[rows], o_ref, lse_ref,
+                  f"graph batch={batch}")
