@@ -185,7 +185,22 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
     }
   }
   __syncthreads();
-  if (live) {
+  if (pp.batch <= 64) {
+    if (b < 64) {  // wave 0 holds every request: bases by a scan, ranks by lane reads
+      const int32_t sb = live ? s_splits[b] : 0;
+      const int32_t cb = live ? s_chunk[b] : 0;
+      const int32_t base = (int32_t)wave_scan((uint32_t)sb) - sb;
+      int32_t rank = 0;
+      for (int i = 0; i < pp.batch; ++i) {
+        const int32_t ci = __builtin_amdgcn_readlane(cb, i);
+        rank += (ci > cb || (ci == cb && i < b)) ? 1 : 0;
+      }
+      if (live) {
+        out->part_base[b] = (uint32_t)base;
+        s_order[rank] = b;
+      }
+    }
+  } else if (live) {
     int32_t base = 0, rank = 0;
     for (int i = 0; i < pp.batch; ++i) {
       if (i < b) base += s_splits[i];
