@@ -98,42 +98,49 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
   int32_t L = 0;
   if (live) L = min(max(kv_lens[b], 0), pp.max_kv_len);
   const int64_t pages = ((int64_t)L + kPage - 1) / kPage;
-  {
+  // Up to 64 requests, every wave holds all of them (lane = request) and reduces and
+  // searches on its own, with no barrier; beyond that the waves' sums meet in LDS. All
+  // sums are of integers, so both ways give the same plan.
+  const bool one_wave = pp.batch <= 64;
+  const int lane = b & 63;
+  uint32_t ps32 = (uint32_t)pages;  // pages of the request this lane searches with
+  bool s_live = live;
+  if (one_wave) {
+    s_live = lane < pp.batch;
+    const int32_t Ll = s_live ? min(max(kv_lens[lane], 0), pp.max_kv_len) : 0;
+    ps32 = (uint32_t)(((int64_t)Ll + kPage - 1) / kPage);
+  }
+  int64_t total_pages = 0;
+  int32_t maxp = 1;
+  if (one_wave) {
+    // pages <= 2^26: the low and high 16 bits summed apart cannot overflow 32 bits
+    maxp = max(1, wave_max(s_live ? (int32_t)ps32 : 1));
+    const uint32_t lo16 = (uint32_t)wave_sum((int32_t)(ps32 & 0xFFFFu));
+    const uint32_t hi16 = (uint32_t)wave_sum((int32_t)(ps32 >> 16));
+    total_pages = (int64_t)lo16 + ((int64_t)hi16 << 16);
+  } else {
     const int32_t pm = wave_max(live ? (int32_t)pages : 1);   // pages <= 2^26
     const long long ps = wave_sum64(live ? pages : 0);        // up to 64 x 2^26
     if ((b & 63) == 0) {
       s_pmax[b >> 6] = pm;
       s_psum[b >> 6] = ps;
     }
-  }
-  __syncthreads();
-  int64_t total_pages = 0;
+    __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kPlanWaves; ++w) total_pages += s_psum[w];
+    for (int w = 0; w < kPlanWaves; ++w) {
+      total_pages += s_psum[w];
+      maxp = max(maxp, s_pmax[w]);
+    }
+  }
 
   // proportional plan: the smallest split length C (pages) with
   // sum_b clamp(ceil(pages_b / C), 1, cap) <= budget; every thread runs the same search
   int64_t C = 1;
   if (pp.split_kv <= 0) {
     const int64_t Bn = pp.batch, budget = pp.budget;
-    int32_t maxp = 1;
-#pragma unroll
-    for (int w = 0; w < kPlanWaves; ++w) maxp = max(maxp, s_pmax[w]);
     int64_t lo = 1, hi = maxp;
     if (budget > Bn) hi = min(hi, (total_pages + (budget - Bn) - 1) / (budget - Bn));
     else lo = hi;
-    // Up to 64 requests, every wave holds all of them (lane = request) and runs the
-    // search on its own, with no barrier per step; beyond that the waves' sums meet in
-    // LDS. Both orders of summation are exact (integers), so the plan is the same.
-    const bool one_wave = pp.batch <= 64;
-    const int lane = b & 63;
-    uint32_t ps32 = (uint32_t)pages;
-    bool s_live = live;
-    if (one_wave) {
-      s_live = lane < pp.batch;
-      const int32_t Ll = s_live ? min(max(kv_lens[lane], 0), pp.max_kv_len) : 0;
-      ps32 = (uint32_t)(((int64_t)Ll + kPage - 1) / kPage);
-    }
     while (lo < hi) {
       const int64_t mid = lo + (hi - lo) / 2;  // <= max pages < 2^27: 32-bit division
       const uint32_t m32 = (uint32_t)mid;
