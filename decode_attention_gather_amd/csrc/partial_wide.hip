@@ -478,7 +478,7 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   }
 
   // one step: O += P~ V over the stage's two pages, with the direct-to-LDS loads of
-  // step st + 2 (when dma) issued between the MFMAs
+  // step st + 2 (when dma) issued together after the first dim tile's MFMAs
   auto pv_step = [&](int st, bool dma, uint64_t gp) {
     const int pb = st & 1;
     int sa[kRT];
@@ -545,7 +545,10 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
 #pragma unroll
       for (int k = 0; k < kRT; ++k)
         acc[k][d] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[k], vb, acc[k][d], 0, 0, 0, sa[k], 0, 127);
-      if (d < R::kDMA && dma) issue_one(gp, dst, d);
+      if (d == 0 && dma) {  // the step's loads go out together, after the first MFMAs
+#pragma unroll
+        for (int i = 0; i < R::kDMA; ++i) issue_one(gp, dst, i);
+      }
     }
   };
 
