@@ -64,12 +64,12 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
   return min(max(e, -127), 127);
 }
 
-struct MergeSmem {
-  float o[kMaxGroups][kDV];
-  float m[kMaxGroups];
-  float l[kMaxGroups];
-  float lt[kMaxGroups];
-};
+// Dynamic shared memory of a merge workgroup, sized by the launch's group count G (a
+// workgroup of one wave needs 2 KB, not the 32 KB of 16 groups, so more of them fit on a
+// CU): o[G][dims of the slice], then m[G], l[G], l~[G].
+inline size_t merge_smem_bytes(int groups, int slices) {
+  return (size_t)groups * (size_t)(kDV / slices + 3) * sizeof(float);
+}
 
 // kDev: the plan and output_scale come from device memory (graph path).
 template <bool kF32Out, bool kDev, int kW>
@@ -78,11 +78,15 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
              const float* __restrict__ oscale_dev, const float* __restrict__ ws_o,
              const float* __restrict__ ws_stats, float output_scale_arg, void* __restrict__ out,
              float* __restrict__ lse, int groups, const MergeEpilogue ep) {
-  __shared__ MergeSmem sm;
+  extern __shared__ __attribute__((aligned(16))) float merge_smem[];
   const PlanDev& P = kDev ? *pdev : Parg;
   const float output_scale = kDev ? *oscale_dev : output_scale_arg;
   constexpr int kD = 8 / kW;                  // dims per lane
   constexpr int kSlice = kDV / kW;            // dims per workgroup
+  float* const so = merge_smem;               // [groups][kSlice]
+  float* const sm_m = so + groups * kSlice;
+  float* const sm_l = sm_m + groups;
+  float* const sm_lt = sm_l + groups;
   // partials in flight per wavefront (4 at W = 1: more registers would halve the
   // workgroups a CU holds, which costs more than the extra loads give)
   constexpr int kU = kW >= 2 ? 16 : 4;
@@ -144,25 +148,25 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
     }
   }
 #pragma unroll
-  for (int i = 0; i < kD; ++i) sm.o[gw][kD * lane + i] = o[i];
+  for (int i = 0; i < kD; ++i) so[gw * kSlice + kD * lane + i] = o[i];
   if (lane == 0) {
-    sm.m[gw] = M;
-    sm.l[gw] = l;
-    sm.lt[gw] = lt;
+    sm_m[gw] = M;
+    sm_l[gw] = l;
+    sm_lt[gw] = lt;
   }
   __syncthreads();
 
   float Mx = -INFINITY;
-  for (int k = 0; k < G; ++k) Mx = fmaxf(Mx, sm.m[k]);
+  for (int k = 0; k < G; ++k) Mx = fmaxf(Mx, sm_m[k]);
   // a sink above every partial's max raises M to its (integer) ceiling
   const float sig = ep.sinks != nullptr ? ep.sinks[r % P.heads] * kLog2e : -INFINITY;
   if (sig > Mx) Mx = ceilf(sig);
   float wk[kMaxGroups];
   float L = 0.f, Lt = 0.f;
   for (int k = 0; k < G; ++k) {
-    wk[k] = Mx == -INFINITY ? 0.f : pow2i(sm.m[k], Mx);
-    L += wk[k] * sm.l[k];
-    Lt += wk[k] * sm.lt[k];
+    wk[k] = Mx == -INFINITY ? 0.f : pow2i(sm_m[k], Mx);
+    L += wk[k] * sm_l[k];
+    Lt += wk[k] * sm_lt[k];
   }
   if (sig > -INFINITY) {
     const float ps = exp2f(sig - Mx + 8.f);
@@ -173,7 +177,7 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   if (kF32Out || ep.o_fp8 == nullptr) {
     for (int d = threadIdx.x; d < kSlice; d += blockDim.x) {
       float acc = 0.f;
-      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][d];
+      for (int k = 0; k < G; ++k) acc += wk[k] * so[k * kSlice + d];
       const float v = acc * inv;
       if (kF32Out)
         ((float*)out)[(int64_t)row_global * kDV + dim0 + d] = v;
@@ -182,7 +186,7 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
     }
   } else if (threadIdx.x < kSlice / 8) {
     // MXFP8 (and BF16 when out is given): lane t owns dims dim0 + 8t .. dim0 + 8t + 7
-    const int dl = 8 * (int)threadIdx.x;  // in the slice (sm.o)
+    const int dl = 8 * (int)threadIdx.x;  // in the slice (so)
     const int d0 = dim0 + dl;             // in the row
     float vb[8];
     uint32_t hw[4];
@@ -190,7 +194,7 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float acc = 0.f;
-      for (int k = 0; k < G; ++k) acc += wk[k] * sm.o[k][dl + i];
+      for (int k = 0; k < G; ++k) acc += wk[k] * so[k * kSlice + dl + i];
       const uint16_t h16 = f32_to_bf16_rne(acc * inv);
       vb[i] = __uint_as_float((uint32_t)h16 << 16);
       amax = fmaxf(amax, fabsf(vb[i]));
@@ -237,7 +241,7 @@ int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* 
   const dim3 grid(rows_total * W), block(64 * groups);
   // one instantiation per (output type, plan source, slices)
 #define MLA_MERGE_LAUNCH(F32, DEV, KW) \
-  hipLaunchKernelGGL((merge_kernel<F32, DEV, KW>), grid, block, 0, st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep)
+  hipLaunchKernelGGL((merge_kernel<F32, DEV, KW>), grid, block, merge_smem_bytes(groups, KW), st, P, pd, od, ws_o, ws_stats, output_scale, o, lse, groups, ep)
 #define MLA_MERGE_W(F32, DEV)                      \
   switch (W) {                                     \
     case 1: MLA_MERGE_LAUNCH(F32, DEV, 1); break;  \
