@@ -45,8 +45,9 @@ def _load(path: str | None = None):
     """Load the oracle library (or a variant built elsewhere, for mutation tests)."""
     key = path or _LIB_PATH
     if key not in _libs:
-        if path is None and not os.path.exists(_LIB_PATH):
-            build(force=True)
+        if path is None and (not os.path.exists(_LIB_PATH) or
+                             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build(force=True)  # missing, or older than its source
         lib = ctypes.CDLL(key)
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]

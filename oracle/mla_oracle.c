@@ -60,14 +60,22 @@
  * sigma_h = -inf gives back the definition without a sink.
  *
  * MXFP8 output [TensorRT-LLM PR #17441 "m3 decode perf clean", the commit messages on
- * the MXFP8 quantize-tile epilogue and the sparse decode merge: the merge emits E4M3
- * values with UE8M0 block scales next to the BF16 O it stores, bit-identical to
- * quantizing that BF16 tensor afterwards]: blocks of 32 consecutive elements of a row; the block's
- * scale is amax / 448 rounded up to a power of two 2^e (the smallest integer e with
- * amax <= 448 * 2^e), clamped to the E8M0 range [-127, 127] and stored as e + 127; each
- * element is the E4M3 value nearest to x / 2^e, ties to the even code, with the sign
- * of x. Here e is found exactly; the pages' implementation reaches it through an
- * approximate reciprocal of 448, which can give e + 1 when amax is 1.75 * 2^k.
+ * the MXFP8 quantize-tile epilogue, on its scale byte 0, and on the sparse decode merge:
+ * the merge emits E4M3 values with UE8M0 block scales next to the BF16 O it stores,
+ * bit-identical to quantizing that BF16 tensor afterwards]: blocks of 32 consecutive
+ * elements of a row. The block scale is amax / 448 rounded up to a power of two, with
+ * the outcome those messages state for the two edge cases:
+ *   - a block whose amax is exactly 1.75 * 2^k (= 448 * 2^(k-8)) gets the next
+ *     exponent, k - 7: the scale is 2^e with e the smallest integer such that
+ *     amax < 448 * 2^e (strictly), clamped to the E8M0 range [-127, 127] and stored
+ *     as e + 127;
+ *   - a block whose scale byte is 0 (e = -127: amax < 448 * 2^-127, including an
+ *     all-zero block) saturates: the reciprocal of its scale is taken as infinite, so
+ *     every non-zero element becomes the largest E4M3 magnitude, 448, with its sign.
+ *     A zero element has no magnitude to saturate and stays a zero code with its sign
+ *     (a reading: the messages say only that the block saturates).
+ * Otherwise each element is the E4M3 value nearest to x / 2^e, ties to the even code,
+ * with the sign of x (|x / 2^e| < 448, so nothing else saturates).
  *
  * Threads: rows are handed out to POSIX threads through an atomic counter; each row's
  * arithmetic is sequential and independent of the thread count.
@@ -367,11 +375,20 @@ int oracle_mxfp8_quantize(const double* x, int64_t nrows, uint8_t* codes, uint8_
         if (!isfinite(xb[i])) return ORACLE_ERR_ARG;
         if (fabs(xb[i]) > amax) amax = fabs(xb[i]);
       }
+      /* smallest e with amax < 448 * 2^e, within the E8M0 range */
       int e = -127;
-      while (e < 127 && amax > ldexp(448.0, e)) ++e;
+      while (e < 127 && amax >= ldexp(448.0, e)) ++e;
       scales[r * (ORACLE_D_V / block) + blk] = (uint8_t)(e + 127);
-      for (int i = 0; i < block; ++i)
-        codes[r * ORACLE_D_V + blk * block + i] = e4m3_nearest(ldexp(xb[i], -e));
+      for (int i = 0; i < block; ++i) {
+        uint8_t* c = &codes[r * ORACLE_D_V + blk * block + i];
+        if (e == -127) {
+          /* scale byte 0: the block saturates; zeros stay zeros */
+          uint8_t neg = signbit(xb[i]) ? 0x80 : 0x00;
+          *c = (uint8_t)(neg | (xb[i] != 0.0 ? 0x7E : 0x00));
+        } else {
+          *c = e4m3_nearest(ldexp(xb[i], -e));
+        }
+      }
     }
   }
   return 0;

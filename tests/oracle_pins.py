@@ -330,46 +330,71 @@ def _mx_blocks(seed):
     x[32:64] = 448.0 * 2.0 ** 5                        # 448 * 2^5
     x[64] = 448.0 * (1 + 2.0 ** -7)                    # next BF16 above 448
     x[96] = 1.75                                      # 448 * 2^-8
-    x[128] = 1.875                                    # just above: one exponent up
+    x[128] = 1.875                                    # just above
     x[160:192] = -g.random(32) * 3.0                  # negative block
     x[192:224] = 0.0                                  # all zero
     x[224] = -0.0
     x[256:288] = np.ldexp(1.0 + np.arange(32) / 8.0, -3)
+    x[288] = 1.7421875                                # the BF16 value just below 1.75
+    x[289] = -0.0                                     # -0 in a block that is not saturated
     rows.append(x)
+    y = np.zeros(512)                                 # the low end of the E8M0 range
+    y[0:4] = [2.0 ** -125, -2.0 ** -130, 0.0, -0.0]   # scale byte 0: the block saturates
+    y[32] = 1.75 * 2.0 ** -119                        # = 448 * 2^-127: scale byte 1
+    y[33] = -2.0 ** -133
+    y[64] = 1.7421875 * 2.0 ** -119                   # just below: scale byte 0
+    y[65] = -0.0
+    y[96] = 2.0 ** -133                               # the smallest BF16 subnormal
+    rows.append(y)
     return oracle.round_bf16(np.stack(rows))
 
 
 def pin_mxfp8(lib_path=None):
-    """MXFP8 of BF16 rows: every scale is the smallest power of two 2^e with
-    amax <= 448 * 2^e (from frexp, a different route), clamped to [-127, 127]; every
-    element is torch's RNE float8_e4m3fn cast of x / 2^e; hand cases pin the edges."""
+    """MXFP8 of BF16 rows (PR #17441 "m3 decode perf clean", commit messages on the MXFP8
+    quantize tile and on its scale byte 0): every scale is the smallest power of two 2^e
+    with amax < 448 * 2^e, strictly, so amax = 1.75 * 2^k takes the next exponent (from
+    frexp, a different route), clamped to [-127, 127]; a block of scale byte 0 saturates
+    (non-zero elements to +-448, zeros stay zeros); every other element is torch's RNE
+    float8_e4m3fn cast of x / 2^e; hand cases pin the edges."""
     x = _mx_blocks(41)
     codes, scales = oracle.mxfp8_quantize(x, lib_path)
     xb = x.reshape(x.shape[0], 16, 32)
     amax = np.abs(xb).max(axis=2)
-    # frexp: amax = f * 2^k with f in [0.5, 1); 448 = 0.875 * 2^9
+    # frexp: amax = f * 2^k with f in [0.5, 1); 448 = 0.875 * 2^9, so amax < 448 * 2^e
+    # first holds at e = k - 9 when f < 0.875, else at e = k - 8
     f, k = np.frexp(amax)
-    e_ref = np.where(f <= 0.875, k - 9, k - 8)
+    e_ref = np.where(f < 0.875, k - 9, k - 8)
     e_ref = np.where(amax == 0, -127, np.clip(e_ref, -127, 127))
     assert np.array_equal(scales.astype(np.int64) - 127, e_ref), "block scales"
     y = xb / np.ldexp(1.0, e_ref)[:, :, None]
     ref = torch.from_numpy(y.reshape(x.shape).astype(np.float32)).to(torch.float8_e4m3fn)
-    ref = ref.view(torch.uint8).numpy()
+    ref = ref.view(torch.uint8).numpy().reshape(xb.shape)
+    sat = np.where(xb != 0, 0x7E, 0x00) | np.where(np.signbit(xb), 0x80, 0x00)
+    ref = np.where((e_ref == -127)[:, :, None], sat, ref).astype(np.uint8).reshape(x.shape)
     assert np.array_equal(codes, ref), np.argwhere(codes != ref)[:5]
-    last = codes[-1]
-    assert scales[-1, 0] == 127 and (last[0:32] == 0x7E).all()       # 448 -> code 0x7E
-    assert scales[-1, 1] == 132 and (last[32:64] == 0x7E).all()
-    assert scales[-1, 2] == 128 and last[64] == 0x76                 # 452 / 2 = 226 -> 224
-    assert scales[-1, 3] == 119 and last[96] == 0x7E                 # 1.75 = 448 * 2^-8
-    assert scales[-1, 4] == 120                                      # 1.875 > 1.75
-    assert scales[-1, 6] == 0 and (last[192:224] == 0).all()         # zero block: e = -127
-    assert last[224] == 0x80                                         # -0 keeps its sign
-    # dequantization error: at most half an E4M3 step of x / 2^e
+    hand, low = codes[-2], codes[-1]
+    sh, sl = scales[-2], scales[-1]
+    assert sh[0] == 128 and (hand[0:32] == 0x76).all()       # 448 -> 2^1, 224 -> code 0x76
+    assert sh[1] == 133 and (hand[32:64] == 0x76).all()
+    assert sh[2] == 128 and hand[64] == 0x76                 # 452 / 2 = 226 -> 224
+    assert sh[3] == 120 and hand[96] == 0x76                 # 1.75 = 448 * 2^-8 -> 2^-7
+    assert sh[4] == 120                                      # 1.875 > 1.75
+    assert sh[6] == 0 and (hand[192:224] == 0).all()         # zero block: byte 0, zeros
+    assert hand[224] == 0x80                                 # -0 keeps its sign
+    assert sh[9] == 119 and hand[288] == 0x7E                # 1.7421875 < 1.75: 2^-8, 446 -> 448
+    assert hand[289] == 0x80
+    assert sl[0] == 0 and list(low[0:4]) == [0x7E, 0xFE, 0x00, 0x80]   # saturated block
+    assert sl[1] == 1 and low[32] == 0x76                    # 1.75 * 2^-119 -> 2^-126
+    assert sl[2] == 0 and low[64] == 0x7E and low[65] == 0x80
+    assert sl[3] == 0 and low[96] == 0x7E                    # smallest subnormal saturates
+    # dequantization error: at most half an E4M3 step of x / 2^e (unsaturated blocks)
+    live = e_ref > -127
     deq = oracle.e4m3_table(lib_path)[codes].reshape(xb.shape) * np.ldexp(1.0, e_ref)[:, :, None]
     ya = np.abs(y)
     step = np.where(ya >= 2.0 ** -6, np.ldexp(1.0, np.floor(np.log2(np.maximum(ya, 1e-300))).astype(int) - 3),
                     2.0 ** -9)
-    assert (np.abs(deq - xb) <= 0.5 * step * np.ldexp(1.0, e_ref)[:, :, None] * (1 + 1e-15)).all()
+    ok = np.abs(deq - xb) <= 0.5 * step * np.ldexp(1.0, e_ref)[:, :, None] * (1 + 1e-15)
+    assert ok[live].all()
 
 
 # ---- the BF16 cache variant ---------------------------------------------------------

@@ -33,8 +33,11 @@ MUTANTS = [
      "double r = round(v / quantum) * quantum;"),
     ("bf16_short_significand", "double quantum = ldexp(1.0, e - 7);",
      "double quantum = ldexp(1.0, e - 6);"),
-    ("mx_scale_strict", "while (e < 127 && amax > ldexp(448.0, e)) ++e;",
-     "while (e < 127 && amax >= ldexp(448.0, e)) ++e;"),
+    ("mx_scale_not_strict", "while (e < 127 && amax >= ldexp(448.0, e)) ++e;",
+     "while (e < 127 && amax > ldexp(448.0, e)) ++e;"),
+    ("mx_no_saturation", "if (e == -127) {", "if (0) {"),
+    ("mx_saturate_zeros", "(xb[i] != 0.0 ? 0x7E : 0x00)", "0x7E"),
+    ("mx_saturate_to_nan", "(xb[i] != 0.0 ? 0x7E : 0x00)", "(xb[i] != 0.0 ? 0x7F : 0x00)"),
     ("mx_ties_odd", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
     ("mx_sign_of_zero", "(signbit(y) ? 0x80 : 0)", "(y < 0 ? 0x80 : 0)"),
     ("bf16_bias", "v = ldexp(128.0 + mant, expo - 127 - 7);",
