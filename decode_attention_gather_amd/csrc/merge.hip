@@ -24,10 +24,13 @@
 //     sink is the larger, so the exact power-of-two rescales still apply. LSE is then
 //     the log of the whole denominator.
 //   * MXFP8 O: the BF16 values of O, in blocks of 32 consecutive dims, with an E8M0
-//     scale 2^e, e the smallest integer with amax <= 448 * 2^e (clamped to
-//     [-127, 127]; read off the bits of amax, no division), and E4M3 codes of x / 2^e
-//     (round to nearest even). Four lanes hold one block (8 dims each), so the block
-//     max is two lane swaps.
+//     scale 2^e and E4M3 codes of x / 2^e (round to nearest even). The commit messages
+//     on the quantize tile and its scale byte 0 fix the two edge cases: e is the
+//     smallest integer with amax < 448 * 2^e, strictly (a block whose amax is
+//     1.75 * 2^k gets the exponent above 448's), clamped to [-127, 127] and read off
+//     the bits of amax with no division; and a block of scale byte 0 (e = -127)
+//     saturates: its non-zero elements become +-448, its zeros stay zeros. Four lanes
+//     hold one block (8 dims each), so the block max is two lane swaps.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -55,13 +58,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // E8M0 exponent of an MXFP8 block from its amax (a BF16 value, so exact in fp32): the
-// smallest e with amax <= 448 * 2^e = 1.75 * 2^(e + 8), clamped to [-127, 127].
+// smallest e with amax < 448 * 2^e = 1.75 * 2^(e + 8), strictly, clamped to
+// [-127, 127]. With amax = f 2^k, f in [1, 2): e = k - 8 when f < 1.75, else k - 7.
 __device__ __forceinline__ int mx_block_exponent(float amax) {
   const uint32_t u = __float_as_uint(amax);
   const int ef = (int)((u >> 23) & 0xFF);
   if (ef == 0) return -127;  // zero or below 2^-126: the clamp decides
-  const int e = (ef - 127) - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  const int e = (ef - 127) - 8 + ((u & 0x7FFFFFu) >= 0x600000u ? 1 : 0);
   return min(max(e, -127), 127);
+}
+
+// E4M3 code of a block whose scale byte is 0: the block saturates, so a non-zero value
+// becomes the largest magnitude (code 0x7E) with its sign and a zero stays a zero.
+__device__ __forceinline__ uint32_t mx_saturated_code(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return ((u >> 24) & 0x80u) | ((u & 0x7FFFFFFFu) != 0u ? 0x7Eu : 0u);
 }
 
 // Dynamic shared memory of a merge workgroup, sized by the launch's group count G (a
@@ -217,6 +228,16 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                                              __builtin_amdgcn_ldexpf(vb[5], -e), 0, false);
     c1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(vb[6], -e),
                                          __builtin_amdgcn_ldexpf(vb[7], -e), c1, true);
+    if (e == -127) {  // scale byte 0 (uniform over the block's four lanes)
+      uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s0 |= mx_saturated_code(vb[i]) << (8 * i);
+        s1 |= mx_saturated_code(vb[4 + i]) << (8 * i);
+      }
+      c0 = (int)s0;
+      c1 = (int)s1;
+    }
     *(uint2*)(ep.o_fp8 + (int64_t)row_global * kDV + d0) = make_uint2((uint32_t)c0, (uint32_t)c1);
     if ((threadIdx.x & 3) == 0)
       ep.o_fp8_scales[(int64_t)row_global * (kDV / 32) + (d0 >> 5)] = (uint8_t)(e + 127);

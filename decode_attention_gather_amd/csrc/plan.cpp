@@ -335,6 +335,33 @@ int mla_decode_plan_ex(const int32_t* kv_lens_host, int32_t batch, int32_t q_len
                          num_cus, kv_dtype, out);
 }
 
+int mla_decode_plan_with_merge_bound(const mla_decode_plan_t* plan, int32_t max_groups,
+                                     mla_decode_plan_t** out) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (plan == nullptr || max_groups < 1 || max_groups > 16 || (max_groups & (max_groups - 1)))
+    return MLA_ERR_INVALID_ARG;
+  auto* copy = new (std::nothrow) mla_decode_plan_s(*plan);
+  if (copy == nullptr) return MLA_ERR_NOMEM;
+  copy->kv_lens = nullptr;
+  if (plan->kv_lens != nullptr) {
+    copy->kv_lens = (int32_t*)std::malloc(sizeof(int32_t) * plan->dev.batch);
+    if (copy->kv_lens == nullptr) {
+      delete copy;
+      return MLA_ERR_NOMEM;
+    }
+    std::memcpy(copy->kv_lens, plan->kv_lens, sizeof(int32_t) * plan->dev.batch);
+  }
+  // The planner's width is the largest power of two <= min(16, max S_b), halved while the
+  // launch exceeds its budget; the budget test is monotone in the width, so applying the
+  // bound first and then halving gives min(bound, planner's width). Graph plans: this is
+  // the launch width, which also caps the device planner's choice.
+  copy->merge_groups = std::min(plan->merge_groups, max_groups);
+  copy->dev.groups = std::min<int32_t>(plan->dev.groups, copy->merge_groups);
+  *out = copy;
+  return MLA_OK;
+}
+
 void mla_decode_plan_destroy(mla_decode_plan_t* plan) {
   if (plan == nullptr) return;
   std::free(plan->kv_lens);

@@ -196,3 +196,16 @@ def sample_rows(case: Case, count: int, seed: int = 7) -> List[int]:
             break
         picks.add(int(r))
     return sorted(picks)
+
+
+def sample_rows_per_tile(case: Case, count: int, seed: int = 7) -> List[int]:
+    """sample_rows(case, count) plus one seeded row from every 16-row tile of every
+    request, so that every row block a kernel launch forms is checked."""
+    g = torch.Generator().manual_seed(seed + 1)
+    rows_per_req = case.q_len * case.num_heads
+    picks = set(sample_rows(case, count, seed))
+    for b in range(len(case.kv_lens)):
+        for t0 in range(0, rows_per_req, 16):
+            n = min(16, rows_per_req - t0)
+            picks.add(b * rows_per_req + t0 + int(torch.randint(n, (1,), generator=g)))
+    return sorted(picks)

@@ -29,7 +29,8 @@ D_QK, D_V, PAGE = 576, 512, 32
 EXPORTS = [
     "mla_decode_plan", "mla_decode_plan_ex", "mla_decode_plan_graph",
     "mla_decode_plan_graph_ex", "mla_decode_plan_destroy",
-    "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_partial",
+    "mla_decode_workspace_size", "mla_decode_plan_get_info", "mla_decode_plan_with_merge_bound",
+    "mla_decode_partial",
     "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
     "mla_decode_graph", "mla_decode_merge_ex", "mla_decode_ex", "mla_decode_graph_ex",
     "mla_decode_strerror",
@@ -69,6 +70,8 @@ _lib.mla_decode_graph.restype = ctypes.c_int
 _lib.mla_decode_graph.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _sz, _p, _p, _p]
 _lib.mla_decode_varq.restype = ctypes.c_int
 _lib.mla_decode_varq.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _f32, _f32, _p, _sz, _p, _p, _p]
+_lib.mla_decode_plan_with_merge_bound.restype = ctypes.c_int
+_lib.mla_decode_plan_with_merge_bound.argtypes = [_p, _i32, ctypes.POINTER(_p)]
 _lib.mla_decode_plan_destroy.restype = None
 _lib.mla_decode_plan_destroy.argtypes = [_p]
 _lib.mla_decode_workspace_size.restype = _sz
@@ -170,6 +173,16 @@ class Plan:
         self.q_len = q_len
         self.num_heads = num_heads
         return self
+
+    def with_merge_bound(self, max_groups: int) -> "Plan":
+        """A copy whose merge uses at most max_groups (1, 2, 4, 8, 16) wavefront groups."""
+        other = type(self).__new__(type(self))
+        h = ctypes.c_void_p()
+        _check(_lib.mla_decode_plan_with_merge_bound(self._h, int(max_groups), ctypes.byref(h)),
+               "mla_decode_plan_with_merge_bound")
+        other.__dict__.update({k: v for k, v in self.__dict__.items() if k != "_h"})
+        other._h = h
+        return other
 
     @property
     def handle(self):

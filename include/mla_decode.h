@@ -92,7 +92,8 @@ typedef struct mla_decode_plan_s mla_decode_plan_t;
  *                 (split, row block) work items fill num_cus CUs in one wave, capped at
  *                 max_split_kv (the issue raises that cap to 128 so that a single
  *                 request can occupy the whole GPU);
- *   max_split_kv  cap on splits per request, 1 .. MLA_MAX_SPLIT_KV (128 recommended);
+ *   max_split_kv  cap on splits per request, 1 .. MLA_MAX_SPLIT_KV (the issue uses 128
+ *                 for 148 SMs; 256 lets one request fill the 256 CUs of an MI355X);
  *   num_cus       compute units to fill; 0 = query the current HIP device.
  * Every split holds a whole number of pages and none is empty. Splits are issued
  * longest request first. On success *out owns host memory freed by
@@ -116,6 +117,19 @@ int mla_decode_plan_ex(const int32_t* kv_lens_host, int32_t batch, int32_t q_len
                        int32_t num_cus, int32_t kv_dtype, mla_decode_plan_t** out);
 
 void mla_decode_plan_destroy(mla_decode_plan_t* plan);
+
+/*
+ * A copy of `plan` whose merge folds each row's partials with at most max_groups
+ * wavefront groups (PR #20380, Description: the KvSplit width is an upper bound of 2, 4,
+ * 8 or 16, or 1 for the serial fold, that the host halves until every group holds a
+ * partial and the launch fits its budget). The copy's width is min(max_groups, the
+ * planner's width); everything else is unchanged, so the partial pass is identical and
+ * only the merge's summation order differs. max_groups: 1, 2, 4, 8 or 16, else
+ * MLA_ERR_INVALID_ARG. Works for host and graph plans; *out is freed by
+ * mla_decode_plan_destroy.
+ */
+int mla_decode_plan_with_merge_bound(const mla_decode_plan_t* plan, int32_t max_groups,
+                                     mla_decode_plan_t** out);
 
 /* Bytes of workspace the plan needs (fp32 partials: (512 + 4) * 4 bytes per
  * (row, split)). 0 for a NULL plan. */
@@ -240,7 +254,11 @@ int mla_decode_graph(const mla_decode_plan_t* plan, const void* q, const void* k
  *                 codes of the BF16 O divided by its block scale, nearest even;
  *   o_fp8_scales  device uint8 [B][q_len][H][16]: one E8M0 scale (biased by 127) per 32
  *                 consecutive dims; 2^e with e the smallest integer such that the block's
- *                 largest |BF16 value| <= 448 * 2^e, clamped to [-127, 127].
+ *                 largest |BF16 value| < 448 * 2^e (strictly: an amax of 1.75 * 2^k takes
+ *                 the exponent above, as the commit message on the quantize tile states),
+ *                 clamped to [-127, 127]. A block of scale byte 0 saturates (the commit
+ *                 message on scale byte 0): its non-zero values are coded +-448 (0x7E with
+ *                 the sign), its zeros stay zero codes.
  *                 o_fp8 and o_fp8_scales are given together or not at all.
  *   o             BF16 O as for mla_decode_merge; may be NULL when o_fp8 is given, and
  *                 must be 16-byte aligned when both are written.

@@ -394,3 +394,26 @@ def test_planner_wave_fits_every_xcd(lens, q_len, heads, kv_dtype):
     assert per_xcd <= 32, (info.total_splits, info.row_tiles)
     # and it is not far below one wave: at least 7/8 of the CUs get work
     assert info.work_items >= 0.85 * (32 // info.row_tiles) * 8 * info.row_tiles, info.work_items
+
+
+@pytest.mark.parametrize("lens,q,h,split", [([131072] * 2, 1, 12, 64), ([200000], 1, 12, 200),
+                                            ([131072] * 16, 8, 12, 6), ([5000, 90], 2, 3, 7)])
+def test_merge_bound_copies(lens, q, h, split):
+    """PR #20380 (Description): the merge width is an upper bound of 1, 2, 4, 8 or 16 that
+    the host halves until it fits; the copy keeps every split and only narrows the width."""
+    p = plan(lens, q, h, split, cap=256)
+    info, splits, chunk = p.info()
+    for bound in (1, 2, 4, 8, 16):
+        c = p.with_merge_bound(bound)
+        ci, cs, cc = c.info()
+        assert ci.merge_groups == min(bound, info.merge_groups)
+        assert (cs, cc) == (splits, chunk)
+        assert ci.merge_slices == info.merge_slices and ci.total_splits == info.total_splits
+        assert c.workspace_size() == p.workspace_size()
+    for bad in (0, 3, 32, -1):
+        with pytest.raises(mla.MlaError):
+            p.with_merge_bound(bad)
+    g = mla.Plan.graph(len(lens), q_len=q, num_heads=h, max_kv_len=max(lens), split_kv=split,
+                       num_cus=256)
+    gi = g.info()[0]
+    assert g.with_merge_bound(2).info()[0].merge_groups == min(2, gi.merge_groups)

@@ -114,7 +114,7 @@ def _target_rows(seed, nrows):
     x[0:32] = 448.0
     x[32:64] = -448.0 * 2.0 ** -5
     x[64] = 448.0 * (1 + 2.0 ** -7)                # one BF16 step above 448: e goes up
-    x[96] = 1.75                                   # exactly 448 * 2^-8
+    x[96] = 1.75                                   # exactly 448 * 2^-8: e goes up too
     x[128] = 1.875
     x[160:192] = 0.0
     x[192:224] = -0.0
@@ -122,6 +122,12 @@ def _target_rows(seed, nrows):
     x[256:288] = np.ldexp(1.0 + np.arange(32) / 16.0, 7)   # more ties, other exponent
     rows[1][0:32] = np.ldexp(g.integers(1, 100, 32).astype(np.float64), -140)  # BF16 subnormals
     rows[1][32:64] = np.ldexp(1.0, -126) * (1 + np.arange(32) / 64.0)          # normal floor
+    # the low end of the E8M0 range: amax = 448 * 2^-127 takes scale byte 1; one BF16
+    # step below it, scale byte 0 and the block saturates (zeros stay zeros)
+    rows[1][64:96] = 0.0
+    rows[1][64], rows[1][65] = 1.75 * 2.0 ** -119, -2.0 ** -133
+    rows[1][96:128] = 0.0
+    rows[1][96], rows[1][97], rows[1][98] = 1.7421875 * 2.0 ** -119, -2.0 ** -125, -0.0
     return np.stack(rows).astype(np.float32)
 
 
@@ -159,6 +165,7 @@ def test_mxfp8_synthetic_exact(mla):
         assert np.array_equal(sc.cpu().numpy(), scales), \
             np.argwhere(sc.cpu().numpy() != scales)[:5]
         assert np.array_equal(c.cpu().numpy(), codes), np.argwhere(c.cpu().numpy() != codes)[:5]
+        _check_mx_of_bf16(np_of(o), c.cpu().numpy(), sc.cpu().numpy())  # a second route
     # without the BF16 pointer the MXFP8 pair is unchanged
     c2 = torch.empty_like(c)
     sc2 = torch.empty_like(sc)
@@ -170,15 +177,19 @@ def test_mxfp8_synthetic_exact(mla):
 # ---- MXFP8 on real batches ------------------------------------------------------------
 
 def _check_mx_of_bf16(bf16, codes, scales):
-    """The codes and scales are the MXFP8 quantization of the BF16 values beside them:
-    minimal power-of-two scale per block and the RNE E4M3 cast (torch's) of x / 2^e."""
+    """The codes and scales are the MXFP8 quantization of the BF16 values beside them
+    (PR #17441, commit messages on the quantize tile and its scale byte 0): the smallest
+    power-of-two scale with amax < 448 * 2^e (strictly) per block, the RNE E4M3 cast
+    (torch's) of x / 2^e, and +-448 for the non-zero values of a scale-byte-0 block."""
     xb = bf16.reshape(-1, 16, 32).astype(np.float64)
     e = scales.astype(np.int64).reshape(-1, 16) - 127
     amax = np.abs(xb).max(axis=2)
-    assert (amax <= 448.0 * np.ldexp(1.0, e)).all(), "scale too small"
-    assert ((e == -127) | (amax > 448.0 * np.ldexp(1.0, e - 1))).all(), "scale not minimal"
+    assert (amax < 448.0 * np.ldexp(1.0, e)).all(), "scale too small"
+    assert ((e == -127) | (amax >= 448.0 * np.ldexp(1.0, e - 1))).all(), "scale not minimal"
     y = (xb / np.ldexp(1.0, e)[:, :, None]).reshape(bf16.shape).astype(np.float32)
-    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(xb.shape)
+    sat = np.where(xb != 0, 0x7E, 0x00) | np.where(np.signbit(xb), 0x80, 0x00)
+    ref = np.where((e == -127)[:, :, None], sat, ref).astype(np.uint8).reshape(codes.shape)
     assert np.array_equal(codes, ref), np.argwhere(codes != ref)[:5]
 
 

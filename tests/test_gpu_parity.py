@@ -37,7 +37,7 @@ def mla():
     return m
 
 
-def run_gpu(mla, case, split_kv=None, max_split_kv=128, f32_out=False, dc=None):
+def run_gpu(mla, case, split_kv=None, max_split_kv=256, f32_out=False, dc=None):
     dc = dc or mla.to_device(case)
     sk = case.split_kv if split_kv is None else split_kv
     plan = mla.Plan(dc.kv_lens_host, q_len=case.q_len, num_heads=case.num_heads, split_kv=sk,
@@ -85,6 +85,18 @@ SMALL = [
 ]
 
 
+def test_planner_cap_128(mla):
+    """The pages' per-request cap of 128 splits (issue #20510, Repro 2), beside the
+    default 256: a long request hits the cap, parity holds."""
+    case = inputs.make_case([300000, 2000], num_heads=12, q_len=1, seed=77, split_kv=0)
+    _say("[gpu] planner with max_split_kv=128")
+    o, lse, plan = run_gpu(mla, case, max_split_kv=128)
+    assert plan.info()[1][0] == 128
+    rows = inputs.sample_rows(case, 24)
+    o_ref, lse_ref = run_oracle(case, rows)
+    assert_parity(o[rows], lse[rows], o_ref, lse_ref, "cap128")
+
+
 @pytest.mark.parametrize("name,lens,heads,q_len,split", SMALL, ids=[s[0] for s in SMALL])
 def test_small_parity(mla, name, lens, heads, q_len, split):
     case = inputs.make_case(lens, num_heads=heads, q_len=q_len, seed=zlib.crc32(name.encode()) % 10000,
@@ -123,13 +135,20 @@ def test_kv_len_one_and_equal_scores(mla, heads):
     np.testing.assert_allclose(lse, np.log([100.0] * heads + [1000.0] * heads), rtol=1e-6)
 
 
-def test_split_invariance_f32(mla):
-    """fp32 O (before the BF16 cast) from different split plans agrees to 1e-5."""
-    case = inputs.make_case([3000, 20000, 777], num_heads=12, q_len=8, seed=8)
+@pytest.mark.parametrize("lens,heads,q_len", [
+    ([3000, 20000, 777], 12, 8),      # wide kernel, 96-row blocks
+    ([131072, 3000, 777], 12, 1),     # narrow kernel, one row tile (the headline's)
+    ([131072, 3000, 777], 16, 2),     # narrow kernel, two row tiles
+    ([131072, 3000, 777], 12, 2),     # narrow kernel, two row tiles with padding rows
+], ids=["wide_h12_q8", "narrow_h12_q1", "narrow_h16_q2", "narrow_h12_q2"])
+def test_split_invariance_f32(mla, lens, heads, q_len):
+    """fp32 O (before the BF16 cast) from different split plans agrees to 1e-5. Lengths
+    3000 and 777 end inside a page and inside a two-page step, 131072 is the headline's."""
+    case = inputs.make_case(lens, num_heads=heads, q_len=q_len, seed=8)
     dc = mla.to_device(case)
     outs = []
     for sk in (1, 2, 5, 0, 13):
-        _say(f"[gpu] split invariance split_kv={sk}")
+        _say(f"[gpu] split invariance H={heads} q={q_len} split_kv={sk}")
         o, lse, plan = run_gpu(mla, case, split_kv=sk, f32_out=True, dc=dc)
         outs.append((sk, o, lse))
     base = outs[0]
@@ -167,6 +186,44 @@ def test_device_lengths_shorter_than_plan(mla):
                         kv_lens=torch.tensor([200], dtype=torch.int32), q_len=1, num_heads=12)
     o_ref, lse_ref = run_oracle(short)
     assert_parity(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref, "short-device")
+
+
+@pytest.mark.parametrize("lens,heads,q_len,split", [
+    ([200000], 12, 1, 200),        # 8 dim slices per row (one long request)
+    ([131072, 131072], 12, 8, 32),  # wide kernel partials, one slice
+    ([40000, 300, 9000], 12, 2, 0),  # planner, uneven split counts
+], ids=["slices8_q1", "wide_q8_split32", "planner_q2"])
+def test_merge_width_sweep(mla, lens, heads, q_len, split):
+    """PR #20380 (Test Coverage): the same partials merged with KvSplit 2/4/8/16 agree with
+    KvSplit 1. Here: elementwise on the fp32 O and on LSE, to 1e-5."""
+    case = inputs.make_case(lens, num_heads=heads, q_len=q_len, seed=21)
+    dc = mla.to_device(case)
+    plan = mla.Plan(dc.kv_lens_host, q_len=q_len, num_heads=heads, split_kv=split)
+    ws = plan.alloc_workspace()
+    mla.partial(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale, ws)
+    rows = case.rows
+    outs = {}
+    for gmax in (1, 2, 4, 8, 16):
+        p = plan.with_merge_bound(gmax)
+        g = p.info()[0].merge_groups
+        o = torch.empty((rows, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+        mla.merge(p, ws, dc.output_scale, o, lse)
+        torch.cuda.synchronize()
+        outs[gmax] = (g, o.cpu().numpy(), lse.cpu().numpy())
+        _say(f"[gpu] merge width bound {gmax}: groups {g}, slices {p.info()[0].merge_slices}")
+    assert outs[16][0] >= 8, "the sweep must reach wide merges"
+    _, o1, l1 = outs[1]
+    assert np.isfinite(o1).all() and np.isfinite(l1).all()
+    for gmax in (2, 4, 8, 16):
+        _, o, lse = outs[gmax]
+        d = float(np.abs(o - o1).max())
+        dl = float((np.abs(lse - l1) / np.maximum(1.0, np.abs(l1))).max())
+        _say(f"  KvSplit {gmax} vs 1: max |dO| = {d:.2e}, max |dLSE| rel = {dl:.2e}")
+        assert d <= 1e-5 and dl <= 1e-5, (gmax, d, dl)
+    o_ref, lse_ref = run_oracle(case, inputs.sample_rows(case, 12))
+    assert_parity(o1[inputs.sample_rows(case, 12)], l1[inputs.sample_rows(case, 12)], o_ref,
+                  lse_ref, "width sweep vs oracle")
 
 
 # ---- merge kernel alone, on synthetic partials -------------------------------------
@@ -247,11 +304,12 @@ FULL = ["c1_b1_h12_q1_2k", "c2_b4_h12_q1_128k", "c3_b16_h12_q8_128k", "c4_b1_h12
 def test_full_config_sampled(mla, name):
     _say(f"[gpu] full config {name}: generating inputs")
     case = inputs.make_config(name)
-    rows = inputs.sample_rows(case, 24)
+    rows = inputs.sample_rows_per_tile(case, 24)  # every row block of every request
     dc = mla.to_device(case)
     for sk in ([case.split_kv, 0] if case.split_kv else [0]):
-        _say(f"[gpu] full config {name}: split_kv={sk}")
-        o, lse, plan = run_gpu(mla, case, split_kv=sk, dc=dc)
+        # the benchmark's plans (split cap 256)
+        _say(f"[gpu] full config {name}: split_kv={sk}, {len(rows)} sampled rows")
+        o, lse, plan = run_gpu(mla, case, split_kv=sk, max_split_kv=256, dc=dc)
         assert np.isfinite(o).all() and np.isfinite(lse).all()
         o_ref, lse_ref = run_oracle(case, rows)
         assert_parity(o[rows], lse[rows], o_ref, lse_ref, f"{name} split={sk}")
