@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -81,6 +83,32 @@ int check_epilogue(const mla_decode_plan_s* plan, const void* ws, size_t ws_byte
 
 int hip_status(int e) { return e == (int)hipSuccess ? MLA_OK : MLA_ERR_HIP_BASE - e; }
 
+// Partials scratch of mla_decode_noalloc: one array per GPU, loaded with the library's
+// code object and held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept in scratch_ptr.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return MLA_ERR_HIP_BASE - (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED_SHAPE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return MLA_ERR_HIP_BASE - (int)e;
+    if (p == nullptr) return MLA_ERR_HIP_BASE - (int)hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MLA_OK;
+}
+
 float* ws_o_of(const mla_decode_plan_s* plan, const void* ws) {
   return (float*)((uint8_t*)ws + plan->ws_plan_bytes);
 }
@@ -145,6 +173,32 @@ int mla_decode(const mla_decode_plan_t* plan, const void* q, const void* kv_cach
   if (rc != MLA_OK) return rc;
   return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
                                  output_scale, o, false, lse, stream));
+}
+
+int mla_decode_noalloc(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                       float softmax_scale, float output_scale, void* o, float* lse,
+                       void* stream) {
+  if (plan == nullptr || plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  const size_t need = plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes;
+  if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  int rc = scratch_of_current_device(&ws);
+  if (rc != MLA_OK) return rc;
+  // the same checks and kernels as mla_decode, with the scratch as the workspace; every
+  // partial the merge reads is written by the partial pass of the same call, so nothing
+  // in the scratch needs clearing
+  rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale, ws,
+                     (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  if (rc != MLA_OK) return rc;
+  rc = check_merge(plan, ws, (size_t)MLA_NOALLOC_SCRATCH_BYTES, output_scale, o, lse);
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                 block_table, bt_stride, kv_lens, softmax_scale,
+                                 ws_o_of(plan, ws), ws_stats_of(plan, ws), stream));
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_merge(*plan, ws_o_of(plan, ws), ws_stats_of(plan, ws), output_scale,
+                                 o, false, lse, stream));
 }
 
 int mla_decode_varq(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,

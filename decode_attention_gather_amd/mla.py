@@ -33,7 +33,7 @@ EXPORTS = [
     "mla_decode_partial",
     "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
     "mla_decode_graph", "mla_decode_merge_ex", "mla_decode_ex", "mla_decode_graph_ex",
-    "mla_decode_strerror",
+    "mla_decode_noalloc", "mla_decode_strerror",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -94,6 +94,8 @@ _lib.mla_decode_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _f32, _f32, _p, _p,
 _lib.mla_decode_graph_ex.restype = ctypes.c_int
 _lib.mla_decode_graph_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p, _p,
                                      _p, _p, _p]
+_lib.mla_decode_noalloc.restype = ctypes.c_int
+_lib.mla_decode_noalloc.argtypes = [_p, _p, _p, _p, _i64, _p, _f32, _f32, _p, _p, _p]
 _lib.mla_decode_strerror.restype = ctypes.c_char_p
 _lib.mla_decode_strerror.argtypes = [ctypes.c_int]
 
@@ -259,6 +261,22 @@ def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
                            block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
                            float(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
                            _ptr(lse), _stream(stream)), "mla_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_noalloc(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
+                   output_scale: float, o, lse=None, stream=None):
+    """mla_decode with the library's per-GPU scratch array in place of a workspace (for
+    callers that cannot allocate); calls that overlap on one GPU race."""
+    _check_kv(plan, q, kv_cache)
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o must be bfloat16")
+    _check(_lib.mla_decode_noalloc(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                   block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
+                                   float(output_scale), _ptr(o), _ptr(lse), _stream(stream)),
+           "mla_decode_noalloc")
 
 
 def decode_graph(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale, output_scale,

@@ -41,7 +41,8 @@
  * Threading and streams. A plan is immutable after creation and may be shared by
  * threads. All compute calls are asynchronous on `stream` (a hipStream_t; NULL = the
  * null stream), enqueue nothing else, and never synchronise the host. The library
- * allocates no device memory, keeps no global mutable state, and throws nothing.
+ * allocates no device memory and throws nothing; its only global mutable state is the
+ * per-GPU scratch array of mla_decode_noalloc (below).
  *
  * Errors. Every int-returning call returns MLA_OK (0) or a negative status. Argument,
  * shape and workspace checks run on the host before anything is enqueued, so a failed
@@ -283,6 +284,28 @@ int mla_decode_graph_ex(const mla_decode_plan_t* plan, const void* q, const void
                         const float* output_scale, const float* sinks, void* workspace,
                         size_t workspace_bytes, void* o, float* lse, void* o_fp8,
                         void* o_fp8_scales, void* stream);
+
+/*
+ * For callers that cannot allocate device memory or hand in a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * computation, checks and kernels as mla_decode with a host plan, except that the
+ * partials live in a scratch array of MLA_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library's code object holds on every GPU it runs on, until the process ends. The call
+ * itself allocates nothing; its first call on a device looks up that device's array
+ * (hipGetSymbolAddress) once.
+ *   plan  a host plan (graph plans: MLA_ERR_INVALID_ARG) whose
+ *         mla_decode_workspace_size() is at most MLA_NOALLOC_SCRATCH_BYTES, else
+ *         MLA_ERR_WORKSPACE; every other argument as for mla_decode.
+ * The current HIP device must be the one `stream` belongs to. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on different streams,
+ * or from different host threads) race and give undefined results; calls on one stream
+ * are ordered and safe. Nothing in the array needs clearing between calls.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mla_decode_noalloc(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                       float softmax_scale, float output_scale, void* o, float* lse,
+                       void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mla_decode_strerror(int status);
