@@ -63,6 +63,11 @@ def _load(path: str | None = None):
             p, p, p, p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, ctypes.c_int, p,
             ctypes.c_int64, p, p, ctypes.c_int]
+        lib.oracle_mla_decode_rows_bounded.restype = ctypes.c_int
+        lib.oracle_mla_decode_rows_bounded.argtypes = [
+            p, p, p, p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_double, p, ctypes.c_int, p, p,
+            ctypes.c_int64, p, p, ctypes.c_int]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_round_bf16.restype = None
@@ -103,7 +108,7 @@ def _np(x, dtype):
 def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
                softmax_scale: float, output_scale: float = 1.0, rows=None,
                nthreads: int = 0, lib_path: str | None = None, sinks=None,
-               kv_dtype: str = "e4m3"):
+               kv_dtype: str = "e4m3", kv_bounds=None):
     """Return (O fp64 [nrows, 512], LSE fp64 [nrows]).
 
     q: uint8 E4M3 codes [B, q_len, H, 576]; kv_cache: uint8 [P, 32, 576]
@@ -111,7 +116,9 @@ def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
     block_table: int32 [B, stride]; kv_lens: int32 [B]. ``rows`` lists flat row ids
     r = (b*q_len + j)*H + h (None: every row in order). The scales are used as given
     (pass the fp32-rounded value when the GPU side takes fp32). ``sinks``: per-head
-    sink logits [H] (None: no sink), in the units of the scaled scores.
+    sink logits [H] (None: no sink), in the units of the scaled scores. ``kv_bounds``:
+    int32 [B, 2] per-request key windows [start, end) (None: no window); a row with no
+    visible key gives O = 0 and LSE = -inf (the sink's logit with a sink).
     """
     lib = _load(lib_path)
     assert kv_dtype in ("e4m3", "bf16")
@@ -137,7 +144,19 @@ def mla_decode(q, kv_cache, block_table, kv_lens, *, q_len: int, num_heads: int,
         rows_ptr = rows_arr.ctypes.data
     o = np.empty((nrows, D_V), dtype=np.float64)
     lse = np.empty((nrows,), dtype=np.float64)
-    if sinks is None and not bf16:
+    if kv_bounds is not None:
+        kb = _np(kv_bounds, np.int32).reshape(-1)
+        assert kb.size == 2 * B, "kv_bounds: [B, 2]"
+        sk = None
+        if sinks is not None:
+            sk = np.ascontiguousarray(np.asarray(sinks, dtype=np.float64).reshape(-1))
+            assert sk.size == num_heads, "one sink per head"
+        rc = lib.oracle_mla_decode_rows_bounded(
+            qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
+            num_heads, stride, num_pages, float(softmax_scale), float(output_scale),
+            None if sk is None else sk.ctypes.data, int(bf16), kb.ctypes.data, rows_ptr,
+            nrows, o.ctypes.data, lse.ctypes.data, int(nthreads))
+    elif sinks is None and not bf16:
         rc = lib.oracle_mla_decode_rows(
             qa.ctypes.data, kva.ctypes.data, bt2.ctypes.data, kla.ctypes.data, B, q_len,
             num_heads, stride, num_pages, float(softmax_scale), float(output_scale), rows_ptr,

@@ -77,6 +77,15 @@
  * Otherwise each element is the E4M3 value nearest to x / 2^e, ties to the even code,
  * with the sign of x (|x / 2^e| < 448, so nothing else saturates).
  *
+ * Key bounds [issue #20510, Repro 1: kv_bounds is one of the run() arguments added
+ * after #19338, named without a description]: read here as one half-open window
+ * [start_b, end_b) of key positions per request, int32 [B][2], that every query of
+ * request b is confined to in addition to the causal rule: query j sees the keys i
+ * with start_b <= i < end_b and i <= L - q_len + j. A negative start counts as 0; keys
+ * outside the window are never read, so block-table entries of pages wholly outside it
+ * may hold anything. A row whose window holds no visible key has O = 0 and
+ * LSE = -inf (LSE = sigma_h with a sink: the sink is then the whole denominator).
+ *
  * Threads: rows are handed out to POSIX threads through an atomic counter; each row's
  * arithmetic is sequential and independent of the thread count.
  */
@@ -133,6 +142,7 @@ typedef struct {
   int64_t bt_stride, num_pages;
   double softmax_scale, output_scale;
   const double* sinks; /* [heads] extra logits, or NULL */
+  const int32_t* bounds; /* [batch][2] key windows [start, end), or NULL */
   int bf16;            /* 0: E4M3 elements (1 byte), 1: BF16 elements (2 bytes) */
   double* table16;     /* BF16 decode table (65536 entries) when bf16 */
   const int64_t* rows;
@@ -170,9 +180,16 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
   int32_t b = (int32_t)(bj / J->q_len);
   int32_t j = (int32_t)(bj % J->q_len);
   int64_t L = J->kv_lens[b];
-  int64_t n = L - J->q_len + j + 1; /* keys visible to query token j */
+  int64_t n = L - J->q_len + j + 1; /* causal rule: query token j sees keys 0 .. n-1 */
   if (n < 1) return ORACLE_ERR_ARG;
   if ((n + ORACLE_PAGE - 1) / ORACLE_PAGE > J->bt_stride) return ORACLE_ERR_ARG;
+  /* keys of the row: [k0, k1), the causal range cut to the request's window */
+  int64_t k0 = 0, k1 = n;
+  if (J->bounds) {
+    int64_t start = J->bounds[2 * (int64_t)b], end = J->bounds[2 * (int64_t)b + 1];
+    if (start > k0) k0 = start;
+    if (end < k1) k1 = end;
+  }
 
   const int64_t row_bytes = (int64_t)ORACLE_D_QK * (J->bf16 ? 2 : 1);
   double qd[ORACLE_D_QK], kd[ORACLE_D_QK];
@@ -180,7 +197,7 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
 
   /* scores s_i = softmax_scale * (q . K_i) */
   double m = -INFINITY;
-  for (int64_t i = 0; i < n; ++i) {
+  for (int64_t i = k0; i < k1; ++i) {
     int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
     if (page < 0 || page >= J->num_pages) return ORACLE_ERR_PAGE;
     decode_row(J, J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * row_bytes, kd);
@@ -195,7 +212,7 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
   /* weights, normaliser, and the weighted sum of V (the first 512 bytes of each row) */
   for (int d = 0; d < ORACLE_D_V; ++d) acc[d] = 0.0;
   double l = J->sinks ? exp(sigma - m) : 0.0;
-  for (int64_t i = 0; i < n; ++i) {
+  for (int64_t i = k0; i < k1; ++i) {
     int64_t page = J->bt[(int64_t)b * J->bt_stride + i / ORACLE_PAGE];
     decode_row(J, J->kv + (page * ORACLE_PAGE + i % ORACLE_PAGE) * row_bytes, kd);
     double w = exp(s[i] - m);
@@ -203,6 +220,11 @@ static int one_row(oracle_job* J, int64_t idx, double* s, double* acc) {
     for (int d = 0; d < ORACLE_D_V; ++d) acc[d] += w * kd[d]; /* V: the first 512 */
   }
   double* o = J->out_o + idx * ORACLE_D_V;
+  if (l == 0.0) { /* no visible key and no sink */
+    for (int d = 0; d < ORACLE_D_V; ++d) o[d] = 0.0;
+    J->out_lse[idx] = -INFINITY;
+    return 0;
+  }
   for (int d = 0; d < ORACLE_D_V; ++d) o[d] = J->output_scale * acc[d] / l;
   J->out_lse[idx] = m + log(l);
   return 0;
@@ -257,12 +279,13 @@ static void* worker(void* arg) {
  * nthreads <= 0 uses every online core. Returns 0 or a negative error code; on error
  * the outputs are unspecified.
  */
-int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
-                              const int32_t* kv_lens, int32_t batch, int32_t q_len,
-                              int32_t num_heads, int64_t bt_stride, int64_t num_pages,
-                              double softmax_scale, double output_scale, const double* sinks,
-                              int bf16, const int64_t* rows, int64_t nrows, double* out_o,
-                              double* out_lse, int nthreads) {
+int oracle_mla_decode_rows_bounded(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
+                                   const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                                   int32_t num_heads, int64_t bt_stride, int64_t num_pages,
+                                   double softmax_scale, double output_scale,
+                                   const double* sinks, int bf16, const int32_t* kv_bounds,
+                                   const int64_t* rows, int64_t nrows, double* out_o,
+                                   double* out_lse, int nthreads) {
   if (!q || !kv || !bt || !kv_lens || !out_o || !out_lse) return ORACLE_ERR_ARG;
   if (batch < 1 || q_len < 1 || num_heads < 1 || bt_stride < 1 || num_pages < 1 || nrows < 0)
     return ORACLE_ERR_ARG;
@@ -280,6 +303,7 @@ int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t
   J->softmax_scale = softmax_scale;
   J->output_scale = output_scale;
   J->sinks = sinks;
+  J->bounds = kv_bounds;
   J->bf16 = bf16 ? 1 : 0;
   J->rows = rows;
   J->nrows = nrows;
@@ -309,6 +333,18 @@ int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t
   free(J->table16);
   free(J);
   return rc;
+}
+
+/* The same without key bounds. */
+int oracle_mla_decode_rows_ex(const uint8_t* q, const uint8_t* kv, const int32_t* bt,
+                              const int32_t* kv_lens, int32_t batch, int32_t q_len,
+                              int32_t num_heads, int64_t bt_stride, int64_t num_pages,
+                              double softmax_scale, double output_scale, const double* sinks,
+                              int bf16, const int64_t* rows, int64_t nrows, double* out_o,
+                              double* out_lse, int nthreads) {
+  return oracle_mla_decode_rows_bounded(q, kv, bt, kv_lens, batch, q_len, num_heads, bt_stride,
+                                        num_pages, softmax_scale, output_scale, sinks, bf16,
+                                        NULL, rows, nrows, out_o, out_lse, nthreads);
 }
 
 /* The same without sinks. */

@@ -397,6 +397,121 @@ def pin_mxfp8(lib_path=None):
     assert ok[live].all()
 
 
+# ---- key windows (kv_bounds) ------------------------------------------------------------
+
+def _rebuilt_request(case, b, k0, k1, j):
+    """A one-request, q_len = 1 case holding only the cached tokens k0 .. k1-1 of request
+    b (gathered with torch indexing into fresh pages) and query token j of b."""
+    tok = torch.arange(k0, k1)
+    pages = case.block_table[b].to(torch.int64)[tok // inputs.PAGE]
+    rows = case.kv[pages, tok % inputs.PAGE]
+    n = k1 - k0
+    npg = (n + inputs.PAGE - 1) // inputs.PAGE
+    kv = torch.zeros((npg, inputs.PAGE, inputs.D_QK), dtype=case.kv.dtype)
+    kv.view(-1, inputs.D_QK)[:n] = rows
+    return inputs.Case(q=case.q[b:b + 1, j:j + 1].clone(), kv=kv,
+                       block_table=torch.arange(npg, dtype=torch.int32)[None],
+                       kv_lens=torch.tensor([n], dtype=torch.int32), q_len=1,
+                       num_heads=case.num_heads, output_scale=case.output_scale,
+                       kv_dtype=case.kv_dtype)
+
+
+def _windows_case(kv_dtype="e4m3"):
+    case = inputs.make_case([300, 97, 1000, 64], num_heads=3, q_len=4, seed=61,
+                            output_scale=0.8, kv_dtype=kv_dtype)
+    # page-unaligned starts and ends, a window past the causal frontier, one past L, one
+    # whole request, one that only some queries reach, and an empty one
+    bounds = torch.tensor([[37, 250], [-5, 500], [512, 998], [70, 70]], dtype=torch.int32)
+    return case, bounds
+
+
+def pin_kv_bounds_rebuilt(lib_path=None):
+    """[issue #20510, Repro 1: kv_bounds] A row confined to [start, end) equals, bit for
+    bit, the unbounded oracle on a cache rebuilt (by torch indexing) from just the keys it
+    may see, start .. min(end, L - q_len + j + 1) - 1. Block-table entries of pages wholly
+    outside every window point at a NaN page, which must never be read."""
+    for dt in ("e4m3", "bf16"):
+        case, bounds = _windows_case(dt)
+        bt = case.block_table.clone()
+        nan_page = case.kv.shape[0] - 1          # the poison page of make_case
+        for b in range(case.batch):
+            lo = max(0, int(bounds[b, 0]))
+            for p in range(bt.shape[1]):
+                if 32 * (p + 1) <= lo:
+                    bt[b, p] = nan_page
+        poisoned = inputs.Case(q=case.q, kv=case.kv, block_table=bt, kv_lens=case.kv_lens,
+                               q_len=case.q_len, num_heads=case.num_heads,
+                               output_scale=case.output_scale, kv_dtype=dt)
+        o, lse = oracle.mla_decode(poisoned.q, poisoned.kv, bt, case.kv_lens, q_len=case.q_len,
+                                   num_heads=case.num_heads, softmax_scale=F32_SCALE,
+                                   output_scale=case.output_scale, lib_path=lib_path,
+                                   kv_dtype=dt, kv_bounds=bounds)
+        assert np.isfinite(o).all(), "a key outside its window was read"
+        H, Q = case.num_heads, case.q_len
+        for b in range(case.batch):
+            L = int(case.kv_lens[b])
+            for j in range(Q):
+                k0 = max(0, int(bounds[b, 0]))
+                k1 = min(int(bounds[b, 1]), L - Q + j + 1)
+                rows = [(b * Q + j) * H + h for h in range(H)]
+                if k1 <= k0:
+                    assert (o[rows] == 0).all() and np.isneginf(lse[rows]).all()
+                    continue
+                sub = _rebuilt_request(case, b, k0, k1, j)
+                o_r, lse_r = _run(sub, lib_path)
+                assert np.array_equal(o[rows], o_r), (dt, b, j)
+                assert np.array_equal(lse[rows], lse_r), (dt, b, j)
+
+
+def pin_kv_bounds_whole_and_empty(lib_path=None):
+    """A window covering every key gives the unbounded result bit for bit; an empty one
+    gives O = 0 and LSE = -inf, or LSE = the sink's logit when the row has a sink."""
+    case = inputs.make_case([300, 97], num_heads=2, q_len=3, seed=62)
+    o0, l0 = _run(case, lib_path)
+    for bounds in ([[0, 300], [0, 97]], [[-7, 10 ** 6], [0, 97]]):
+        o, l = oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=3,
+                                 num_heads=2, softmax_scale=F32_SCALE, lib_path=lib_path,
+                                 kv_bounds=np.array(bounds, np.int32))
+        assert np.array_equal(o, o0) and np.array_equal(l, l0)
+    sinks = np.array([1.5, -2.0])
+    for sk in (None, sinks):
+        o, l = oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=3,
+                                 num_heads=2, softmax_scale=F32_SCALE, lib_path=lib_path,
+                                 sinks=sk, kv_bounds=np.array([[5, 5], [90, 40]], np.int32))
+        assert (o == 0).all()
+        ref = np.full(12, -np.inf) if sk is None else np.tile(sinks, 6)
+        assert np.array_equal(l, ref), l
+
+
+def pin_kv_bounds_mpmath(lib_path=None):
+    """Tiny windows against 50-digit arithmetic (no max subtraction), with the causal
+    frontier inside the window for some queries."""
+    import mpmath
+    mpmath.mp.dps = 50
+    case = inputs.make_case([9, 40], num_heads=2, q_len=3, seed=63, output_scale=0.5)
+    bounds = np.array([[2, 8], [33, 39]], np.int32)
+    o, lse = oracle.mla_decode(case.q, case.kv, case.block_table, case.kv_lens, q_len=3,
+                               num_heads=2, softmax_scale=F32_SCALE, output_scale=0.5,
+                               lib_path=lib_path, kv_bounds=bounds)
+    sc = mpmath.mpf(F32_SCALE)
+    for b in range(2):
+        L = int(case.kv_lens[b])
+        rows_all = _dec(_gather(case, b, L)).tolist()
+        for j in range(3):
+            keys = [i for i in range(L) if bounds[b, 0] <= i < bounds[b, 1] and i <= L - 3 + j]
+            for h in range(2):
+                r = (b * 3 + j) * 2 + h
+                qv = _dec(case.q[b, j, h]).tolist()
+                es = [mpmath.exp(sc * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c)
+                                                  for a, c in zip(qv, rows_all[i]))) for i in keys]
+                tot = mpmath.fsum(es)
+                assert abs(lse[r] - float(mpmath.log(tot))) <= 1e-13 * max(1.0, abs(lse[r]))
+                for d in range(0, inputs.D_V, 11):
+                    ref = float(mpmath.mpf("0.5") *
+                                mpmath.fsum(e * rows_all[i][d] for e, i in zip(es, keys)) / tot)
+                    assert abs(o[r, d] - ref) <= 1e-13 * max(1.0, abs(ref)), (b, j, h, d)
+
+
 # ---- the BF16 cache variant ---------------------------------------------------------
 
 def pin_bf16_table(lib_path=None):
@@ -490,5 +605,6 @@ def pin_bf16_mpmath(lib_path=None):
 ALL_PINS = [pin_e4m3_table, pin_single_key, pin_equal_scores, pin_mpmath_bruteforce,
             pin_sdpa, pin_page_permutation, pin_causal_prefix, pin_split_merge,
             pin_bounds_and_dominant, pin_sinks_equal_scores, pin_sinks_logaddexp,
-            pin_sinks_mpmath, pin_bf16_rounding, pin_mxfp8, pin_bf16_table, pin_bf16_sdpa,
+            pin_sinks_mpmath, pin_bf16_rounding, pin_mxfp8, pin_kv_bounds_rebuilt,
+            pin_kv_bounds_whole_and_empty, pin_kv_bounds_mpmath, pin_bf16_table, pin_bf16_sdpa,
             pin_bf16_closed_forms, pin_bf16_mpmath]

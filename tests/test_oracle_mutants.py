@@ -33,6 +33,13 @@ MUTANTS = [
      "double r = round(v / quantum) * quantum;"),
     ("bf16_short_significand", "double quantum = ldexp(1.0, e - 7);",
      "double quantum = ldexp(1.0, e - 6);"),
+    ("bounds_start_off_by_one", "if (start > k0) k0 = start;",
+     "if (start + 1 > k0) k0 = start + 1;"),
+    ("bounds_end_inclusive", "if (end < k1) k1 = end;", "if (end + 1 < k1) k1 = end + 1;"),
+    ("bounds_end_past_causal", "if (end < k1) k1 = end;", "if (end < L) k1 = end;"),
+    ("bounds_of_request_0", "start = J->bounds[2 * (int64_t)b],", "start = J->bounds[0],"),
+    ("empty_row_divides", "if (l == 0.0) { /* no visible key and no sink */",
+     "if (l == -1.0) {"),
     ("mx_scale_not_strict", "while (e < 127 && amax >= ldexp(448.0, e)) ++e;",
      "while (e < 127 && amax > ldexp(448.0, e)) ++e;"),
     ("mx_no_saturation", "if (e == -127) {", "if (0) {"),
