@@ -314,6 +314,78 @@ int mla_decode_graph_ex(const mla_decode_plan_t* plan, const void* q, const void
                                  1.f, o, false, lse, stream, &dev, &ep));
 }
 
+int mla_decode_partial_ex(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                          const int32_t* q_lens, const int32_t* kv_bounds, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if ((q_lens != nullptr && !aligned(q_lens, 4)) || (kv_bounds != nullptr && !aligned(kv_bounds, 4)))
+    return MLA_ERR_INVALID_ARG;
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
+                         workspace, workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  return hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                   block_table, bt_stride, kv_lens, softmax_scale,
+                                   ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                   stream, nullptr, q_lens, kv_bounds));
+}
+
+int mla_decode_bounded(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                       const int32_t* q_lens, const int32_t* kv_bounds, float softmax_scale,
+                       float output_scale, const float* sinks, void* workspace,
+                       size_t workspace_bytes, void* o, float* lse, void* o_fp8,
+                       void* o_fp8_scales, void* stream) {
+  if (plan != nullptr && plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if (kv_bounds == nullptr || !aligned(kv_bounds, 4)) return MLA_ERR_INVALID_ARG;
+  if (q_lens != nullptr && !aligned(q_lens, 4)) return MLA_ERR_INVALID_ARG;
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, softmax_scale,
+                         workspace, workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  rc = check_epilogue(plan, workspace, workspace_bytes, output_scale, o, lse, sinks, o_fp8,
+                      o_fp8_scales);
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache,
+                                 block_table, bt_stride, kv_lens, softmax_scale,
+                                 ws_o_of(plan, workspace), ws_stats_of(plan, workspace), stream,
+                                 nullptr, q_lens, kv_bounds));
+  if (rc != MLA_OK) return rc;
+  const MergeEpilogue ep{sinks, (uint8_t*)o_fp8, (uint8_t*)o_fp8_scales};
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 output_scale, o, false, lse, stream, nullptr, &ep));
+}
+
+int mla_decode_graph_bounded(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                             const int32_t* block_table, int64_t bt_stride,
+                             const int32_t* kv_lens, const int32_t* q_lens,
+                             const int32_t* kv_bounds, const float* softmax_scale,
+                             const float* output_scale, const float* sinks, void* workspace,
+                             size_t workspace_bytes, void* o, float* lse, void* o_fp8,
+                             void* o_fp8_scales, void* stream) {
+  if (plan == nullptr || !plan->device_lengths) return MLA_ERR_INVALID_ARG;
+  if (kv_bounds == nullptr || !aligned(kv_bounds, 4)) return MLA_ERR_INVALID_ARG;
+  if (q_lens != nullptr && !aligned(q_lens, 4)) return MLA_ERR_INVALID_ARG;
+  if (softmax_scale == nullptr || output_scale == nullptr || !aligned(softmax_scale, 4) ||
+      !aligned(output_scale, 4))
+    return MLA_ERR_INVALID_ARG;
+  int rc = check_partial(plan, q, kv_cache, block_table, bt_stride, kv_lens, 1.f, workspace,
+                         workspace_bytes);
+  if (rc != MLA_OK) return rc;
+  rc = check_epilogue(plan, workspace, workspace_bytes, 1.f, o, lse, sinks, o_fp8, o_fp8_scales);
+  if (rc != MLA_OK) return rc;
+  PlanDev* pdev = (PlanDev*)workspace;
+  const DeviceArgs dev{pdev, softmax_scale, output_scale};
+  rc = hip_status(launch_device_plan(*plan, kv_lens, pdev, stream));
+  if (rc != MLA_OK) return rc;
+  rc = hip_status(launch_partial(*plan, (const uint8_t*)q, (const uint8_t*)kv_cache, block_table,
+                                 bt_stride, kv_lens, 1.f, ws_o_of(plan, workspace),
+                                 ws_stats_of(plan, workspace), stream, &dev, q_lens, kv_bounds));
+  if (rc != MLA_OK) return rc;
+  const MergeEpilogue ep{sinks, (uint8_t*)o_fp8, (uint8_t*)o_fp8_scales};
+  return hip_status(launch_merge(*plan, ws_o_of(plan, workspace), ws_stats_of(plan, workspace),
+                                 1.f, o, false, lse, stream, &dev, &ep));
+}
+
 const char* mla_decode_strerror(int status) {
   switch (status) {
     case MLA_OK: return "ok";

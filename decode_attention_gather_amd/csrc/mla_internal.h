@@ -55,6 +55,24 @@ __host__ __device__ inline int chunk_pages_of(const PlanDev& P, int b) {
   return (pages + P.splits[b] - 1) / P.splits[b];
 }
 
+// Keys [*t0, *t1) of split s of request b, whose length (already clamped to the plan's)
+// is L: the split's whole pages cut to [0, L) and, with key windows (kv_bounds: int32
+// [B][2], the window [start_b, end_b) of issue #20510's kv_bounds argument), to the
+// window. An empty range has *t1 == *t0.
+__host__ __device__ inline void split_keys(const PlanDev& P, int b, int s, int L,
+                                           const int32_t* kv_bounds, int* t0, int* t1) {
+  const int chunk = chunk_pages_of(P, b) * kPage;
+  int lo = s * chunk;
+  int hi = lo + chunk < L ? lo + chunk : L;
+  if (kv_bounds != nullptr) {
+    const int wlo = kv_bounds[2 * b], whi = kv_bounds[2 * b + 1];
+    lo = wlo > lo ? wlo : lo;
+    hi = whi < hi ? whi : hi;
+  }
+  *t0 = lo;
+  *t1 = hi > lo ? hi : lo;
+}
+
 }  // namespace mla
 
 // Host-side plan object (opaque to callers). A graph plan (device_lengths != 0) holds
@@ -93,25 +111,28 @@ struct DeviceArgs {
 // Launchers (defined next to their kernels). Return a hipError_t value as int. With
 // dev != nullptr the kernels read the plan and the scales from device memory and the
 // launch is sized by the plan's capacity. q_lens (device, may be null): per-request
-// query tokens of a ragged batch, each clamped to [0, q_len].
+// query tokens of a ragged batch, each clamped to [0, q_len]. kv_bounds (device, may be
+// null): per-request key windows [start, end), int32 [B][2].
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                   const DeviceArgs* dev = nullptr, const int32_t* q_lens = nullptr);
+                   const DeviceArgs* dev = nullptr, const int32_t* q_lens = nullptr,
+                   const int32_t* kv_bounds = nullptr);
 // BF16 cache (rows of 576 BF16 values), blocks of 1 or 2 row tiles.
 int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev, const int32_t* q_lens);
+                        const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds);
 // BF16 cache, blocks of 4 or 6 row tiles.
 int launch_partial_bf16_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                              const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                              float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                             const DeviceArgs* dev, const int32_t* q_lens);
+                             const DeviceArgs* dev, const int32_t* q_lens,
+                             const int32_t* kv_bounds);
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev, const int32_t* q_lens);
+                        const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds);
 // Optional steps of the merge epilogue (any pointer may be null): per-head sink logits
 // (fp32 [H]), and the MXFP8 form of O (E4M3 codes [rows][512], E8M0 scales [rows][16];
 // both or neither). With o_fp8 set, o (BF16) may be null.

@@ -133,7 +133,7 @@ struct Item {
   float* ws_o;
   float* ws_stats;
   float scale_log2;
-  int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int b, part, L, t0, t1, row0, p_first, p_end, nsteps;  // keys [t0, t1), pages [p_first, p_end)
   int qb;  // query tokens of the request (ragged batches), <= q_len
   int lane, w, g, l16;
 };
@@ -147,6 +147,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   const PlanDev& P = *it.P;
   const int lane = it.lane, w = it.w, g = it.g, l16 = it.l16;
   const int nsteps = it.nsteps, p_first = it.p_first, p_end = it.p_end, t1 = it.t1, L = it.L;
+  const int t0 = it.t0;  // a key window can start inside the first page
   const int row0 = it.row0;
 
   // ---------------- QK role: QK^T + softmax of (page w & 1, row tile w >> 1) ----------------
@@ -207,7 +208,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
     }
     // lane holds S[row l16][token 16 tt + 4g + jj] of the page
     const int tok_page = (p_first + st * kStepPages + qk_page) * kPage;
-    const bool need_mask = tok_page + kPage > lim_all;
+    const bool need_mask = tok_page + kPage > lim_all || tok_page < t0;
     float t[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -215,7 +216,8 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         float v = sacc[tt][jj] * it.scale_log2;
-        if (need_mask && tok_page + 16 * tt + 4 * g + jj >= lim_q) v = -INFINITY;
+        const int tok = tok_page + 16 * tt + 4 * g + jj;
+        if (need_mask && (tok >= lim_q || tok < t0)) v = -INFINITY;
         t[tt][jj] = v;
         mx = fmaxf(mx, v);
       }
@@ -361,7 +363,8 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
         acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[rt], ones, acc1, 0, 0, 0, sa[rt], 0, 127);
       }
     }
-    // bytes of tokens past the split's end may be poison: zero them (P~ is 0 there)
+    // bytes of tokens past the split's end, or before a window's start in the first
+    // page, may be poison: zero them (P~ is 0 there)
     uint32_t mk[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
     const bool last = st == nsteps - 1;
     if (last) {
@@ -371,6 +374,15 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
         // byte j of word q4 is token 16 g + 4 q4 + j: the first nb bytes are valid
         const int nb = min(max(valid - (16 * g + 4 * q4), 0), 4);
         mk[q4] = nb >= 4 ? 0xFFFFFFFFu : (1u << (8 * nb)) - 1u;
+      }
+    }
+    if (st == 0 && t0 > p_first * kPage) {
+      const int skip = t0 - p_first * kPage;  // tokens of the step before the window
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // the first nb bytes of word q4 are before the window
+        const int nb = min(max(skip - (16 * g + 4 * q4), 0), 4);
+        mk[q4] &= nb >= 4 ? 0u : ~((1u << (8 * nb)) - 1u);
       }
     }
 #pragma unroll
@@ -463,7 +475,8 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt, int64_t bt_stride,
                const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ q_lens,
-               float scale_log2_arg, float* __restrict__ ws_o, float* __restrict__ ws_stats) {
+               const int32_t* __restrict__ kv_bounds, float scale_log2_arg,
+               float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ Smem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
   const float scale_log2 = kDev ? *scale_dev * 1.4426950408889634f : scale_log2_arg;
@@ -496,13 +509,11 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
-  const int chunk_tok = chunk_pages_of(P, b) * kPage;
-  const int t0 = s * chunk_tok;
-  it.t1 = max(t0, min(t0 + chunk_tok, it.L));
+  split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
-  it.p_first = t0 / kPage;
+  it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
-  it.nsteps = it.t1 > t0 ? (it.p_end - it.p_first + kStepPages - 1) / kStepPages : 0;
+  it.nsteps = it.t1 > it.t0 ? (it.p_end - it.p_first + kStepPages - 1) / kStepPages : 0;
 
   const int w = it.w;
   using R = Roles<NT>;
@@ -516,17 +527,17 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                    const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                    float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                   const DeviceArgs* dev, const int32_t* q_lens) {
+                   const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
   if (plan.kv_dtype == MLA_KV_BF16 && P.nt > kMaxTilesPerBlock)
     return launch_partial_bf16_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o,
-                                    ws_stats, stream, dev, q_lens);
+                                    ws_stats, stream, dev, q_lens, kv_bounds);
   if (plan.kv_dtype == MLA_KV_BF16)
     return launch_partial_bf16(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
-                               stream, dev, q_lens);
+                               stream, dev, q_lens, kv_bounds);
   if (P.nt > kMaxTilesPerBlock)
     return launch_partial_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
-                               stream, dev, q_lens);
+                               stream, dev, q_lens, kv_bounds);
   const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -535,14 +546,14 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   hipStream_t st = (hipStream_t)stream;
   if (P.nt == 1) {
     if (dev)
-      hipLaunchKernelGGL((partial_kernel<1, true>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<1, true>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_kernel<1, false>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<1, false>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   } else {
     if (dev)
-      hipLaunchKernelGGL((partial_kernel<2, true>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<2, true>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_kernel<2, false>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_kernel<2, false>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

@@ -123,7 +123,7 @@ struct BItem {
   float* ws_o;
   float* ws_stats;
   float scale_log2;
-  int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int b, part, L, t0, t1, row0, p_first, p_end, nsteps;  // keys [t0, t1), pages [p_first, p_end)
   int qb;
   int lane, w, g, l16;
 };
@@ -136,6 +136,7 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
   const PlanDev& P = *it.P;
   const int lane = it.lane, w = it.w, g = it.g, l16 = it.l16;
   const int nsteps = it.nsteps, p_first = it.p_first, p_end = it.p_end, t1 = it.t1, L = it.L;
+  const int t0 = it.t0;  // a key window can start inside the first page
   const int row0 = it.row0;
 
   // ---------------- QK role: (row tile w >> 1, token tile w & 1) ----------------
@@ -177,14 +178,14 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
     }
     // lane holds S[row l16][page token 16 tt + 4 g + jj]
     const int tok_page = (p_first + st) * kPage;
-    const bool need_mask = tok_page + kPage > lim_all;
+    const bool need_mask = tok_page + kPage > lim_all || tok_page < t0;
     const int tok0 = tok_page + 16 * qk_tt + 4 * g;
     float t[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       float v = (a0[jj] + a1[jj]) * it.scale_log2;
-      if (need_mask && tok0 + jj >= lim_q) v = -INFINITY;
+      if (need_mask && (tok0 + jj >= lim_q || tok0 + jj < t0)) v = -INFINITY;
       t[jj] = v;
       mx = fmaxf(mx, v);
     }
@@ -313,16 +314,19 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
       }
       pa[rt] = as_bf8(pw);
     }
-    // tokens past the split's end may hold poison: zero their V elements (P~ is 0)
+    // tokens past the split's end, or before a window's start in the first page, may
+    // hold poison: zero their V elements (P~ is 0)
     uint32_t mk[2][2] = {{0xFFFFFFFFu, 0xFFFFFFFFu}, {0xFFFFFFFFu, 0xFFFFFFFFu}};
-    if (st == nsteps - 1) {
+    if (st == nsteps - 1 || (st == 0 && t0 > p_first * kPage)) {
       const int valid = t1 - (p_first + st) * kPage;
+      const int skip = st == 0 ? t0 - p_first * kPage : 0;
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int tk = 16 * r + 4 * g + 2 * h;
-          mk[r][h] = (tk < valid ? 0x0000FFFFu : 0u) | (tk + 1 < valid ? 0xFFFF0000u : 0u);
+          mk[r][h] = (tk < valid && tk >= skip ? 0x0000FFFFu : 0u) |
+                     (tk + 1 < valid && tk + 1 >= skip ? 0xFFFF0000u : 0u);
         }
     }
 #pragma unroll
@@ -405,8 +409,8 @@ partial_bf16_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                     const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                     const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt,
                     int64_t bt_stride, const int32_t* __restrict__ kv_lens,
-                    const int32_t* __restrict__ q_lens, float scale_log2_arg,
-                    float* __restrict__ ws_o, float* __restrict__ ws_stats) {
+                    const int32_t* __restrict__ q_lens, const int32_t* __restrict__ kv_bounds,
+                    float scale_log2_arg, float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ BSmem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
   const float scale_log2 = kDev ? *scale_dev * 1.4426950408889634f : scale_log2_arg;
@@ -439,13 +443,11 @@ partial_bf16_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
-  const int chunk_tok = chunk_pages_of(P, b) * kPage;
-  const int t0 = s * chunk_tok;
-  it.t1 = max(t0, min(t0 + chunk_tok, it.L));
+  split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
-  it.p_first = t0 / kPage;
+  it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
-  it.nsteps = it.t1 > t0 ? it.p_end - it.p_first : 0;
+  it.nsteps = it.t1 > it.t0 ? it.p_end - it.p_first : 0;
 
   const int w = it.w;
   using R = BRoles<NT>;
@@ -459,7 +461,7 @@ partial_bf16_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev, const int32_t* q_lens) {
+                        const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
   const int slots = (P.total_parts + 7) / 8;
   const dim3 grid(8 * slots * P.tiles);
@@ -469,14 +471,14 @@ int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const u
   hipStream_t st = (hipStream_t)stream;
   if (P.nt == 1) {
     if (dev)
-      hipLaunchKernelGGL((partial_bf16_kernel<1, true>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_kernel<1, true>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_bf16_kernel<1, false>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_kernel<1, false>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   } else {
     if (dev)
-      hipLaunchKernelGGL((partial_bf16_kernel<2, true>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_kernel<2, true>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_bf16_kernel<2, false>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_kernel<2, false>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

@@ -185,7 +185,7 @@ struct BWItem {
   float* ws_o;
   float* ws_stats;
   float scale_log2;
-  int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int b, part, L, t0, t1, row0, p_first, p_end, nsteps;  // keys [t0, t1), pages [p_first, p_end)
   int qb;
   int lane, w, g, l16;
 };
@@ -271,7 +271,7 @@ __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           float v = acc[k][tt][jj] * it.scale_log2;
-          if (kMasked && tok0 + jj >= lim_q[k]) v = -INFINITY;
+          if (kMasked && (tok0 + jj >= lim_q[k] || tok0 + jj < it.t0)) v = -INFINITY;
           t[k][tt][jj] = v;
         }
         c[k][tt] = __builtin_elementwise_maximum(  // IEEE maximum: no quieting
@@ -343,7 +343,8 @@ __device__ __forceinline__ void bw_qk(const BWItem& it, BWSmem<NT>& sm) {
     stage_off = stage_off == (kStages - 1) * kPageB ? 0 : stage_off + kPageB;
   };
   auto qk = [&](int st) {
-    if ((p_first + st) * kPage + kPage > lim_all) qk_step(st, std::true_type{});
+    const int tok_page = (p_first + st) * kPage;
+    if (tok_page + kPage > lim_all || tok_page < it.t0) qk_step(st, std::true_type{});
     else qk_step(st, std::false_type{});
   };
 
@@ -406,6 +407,13 @@ __device__ __forceinline__ void bw_pv(const BWItem& it, BWSmem<NT>& sm) {
     if (valid >= kPage) return;
     uint8_t* stage = sm.pages[st % kStages];
     for (int off = valid * kRowB + 16 * (pv * 64 + lane); off < kPageB; off += 16 * 64 * R::kPVW)
+      *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
+  };
+  // rows of the first page before a key window's start read as zero V as well
+  auto zero_head = [&]() {
+    const int skip = it.t0 - p_first * kPage;
+    uint8_t* stage = sm.pages[0];
+    for (int off = 16 * (pv * 64 + lane); off < skip * kRowB; off += 16 * 64 * R::kPVW)
       *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
   };
 
@@ -486,6 +494,7 @@ __device__ __forceinline__ void bw_pv(const BWItem& it, BWSmem<NT>& sm) {
   else wait_vmcnt<0>();
   block_sync_lds();
   if (nsteps == 1) zero_tail(0);
+  if (nsteps > 0) zero_head();
   for (int st = 0; st < nsteps; ++st) {
     // step st + 1 landed; step st + 2's loads may stay in flight
     if (st + 2 < nsteps) wait_vmcnt<kDMA>(); else wait_vmcnt<0>();
@@ -519,7 +528,8 @@ partial_bf16_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                          const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                          const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt,
                          int64_t bt_stride, const int32_t* __restrict__ kv_lens,
-                         const int32_t* __restrict__ q_lens, float scale_log2_arg,
+                         const int32_t* __restrict__ q_lens,
+                         const int32_t* __restrict__ kv_bounds, float scale_log2_arg,
                          float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ BWSmem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
@@ -553,13 +563,11 @@ partial_bf16_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
-  const int chunk_tok = chunk_pages_of(P, b) * kPage;
-  const int t0 = s * chunk_tok;
-  it.t1 = max(t0, min(t0 + chunk_tok, it.L));
+  split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
-  it.p_first = t0 / kPage;
+  it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
-  it.nsteps = it.t1 > t0 ? it.p_end - it.p_first : 0;
+  it.nsteps = it.t1 > it.t0 ? it.p_end - it.p_first : 0;
 
   if (it.w < BWRoles<NT>::kQKW) bw_qk<NT>(it, sm);
   else bw_pv<NT>(it, sm);
@@ -570,7 +578,8 @@ partial_bf16_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial_bf16_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                              const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                              float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                             const DeviceArgs* dev, const int32_t* q_lens) {
+                             const DeviceArgs* dev, const int32_t* q_lens,
+                        const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
   const int slots = (P.total_parts + 7) / 8;
   const dim3 grid(8 * slots * P.tiles);
@@ -581,15 +590,15 @@ int launch_partial_bf16_wide(const mla_decode_plan_s& plan, const uint8_t* q, co
   if (P.nt == 4) {
     const dim3 block(BWRoles<4>::kThreads);
     if (dev)
-      hipLaunchKernelGGL((partial_bf16_wide_kernel<4, true>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_wide_kernel<4, true>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_bf16_wide_kernel<4, false>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_wide_kernel<4, false>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   } else {
     const dim3 block(BWRoles<6>::kThreads);
     if (dev)
-      hipLaunchKernelGGL((partial_bf16_wide_kernel<6, true>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_wide_kernel<6, true>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
-      hipLaunchKernelGGL((partial_bf16_wide_kernel<6, false>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+      hipLaunchKernelGGL((partial_bf16_wide_kernel<6, false>), grid, block, 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

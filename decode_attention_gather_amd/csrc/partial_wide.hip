@@ -193,7 +193,7 @@ struct WItem {
   float* ws_o;
   float* ws_stats;
   float scale_log2;
-  int b, part, L, t1, row0, p_first, p_end, nsteps;
+  int b, part, L, t0, t1, row0, p_first, p_end, nsteps;  // keys [t0, t1), pages [p_first, p_end)
   int qb;  // query tokens of the request (ragged batches), <= q_len
   int lane, w, g, l16;
 };
@@ -292,7 +292,7 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
     auto softmax_page = [&](int p, const v4f (&s0)[kT], const v4f (&s1)[kT]) {
       // lane holds S[row l16][page token 16 tt + 4 g + jj]
       const int tok_page = (p_first + st * kStepPages + p) * kPage;
-      const bool need_mask = tok_page + kPage > lim_all;
+      const bool need_mask = tok_page + kPage > lim_all || tok_page < it.t0;
 #pragma unroll
       for (int k = 0; k < kT; ++k) {
         float t[2][4];
@@ -306,7 +306,9 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-              if (tok_page + 16 * tt + 4 * g + jj >= lim_q[k]) t[tt][jj] = -INFINITY;
+              if (tok_page + 16 * tt + 4 * g + jj >= lim_q[k] ||
+                  tok_page + 16 * tt + 4 * g + jj < it.t0)
+                t[tt][jj] = -INFINITY;
         }
         // IEEE maximum: no quieting of the values that come through the mask branch
         float mx = __builtin_elementwise_maximum(
@@ -460,6 +462,13 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     for (int off = valid * kDQK + 16 * (pv * 64 + lane); off < kStepBytes; off += 16 * 64 * R::kPVW)
       *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
   };
+  // so do the rows of the first page before a key window's start
+  auto zero_head = [&]() {
+    const int skip = it.t0 - p_first * kPage;
+    uint8_t* stage = sm.pages[0];
+    for (int off = 16 * (pv * 64 + lane); off < skip * kDQK; off += 16 * 64 * R::kPVW)
+      *(v4i*)(stage + off) = v4i{0, 0, 0, 0};
+  };
 
   v4f acc[kRT][kDT];
   v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile rt0 + dh: ones product
@@ -561,6 +570,7 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   if (nsteps > 1) wait_vmcnt<R::kDMA>(); else wait_vmcnt<0>();  // step 0 landed
   block_sync_lds();
   if (nsteps == 1) zero_tail(0);
+  if (nsteps > 0) zero_head();
   for (int st = 0; st < nsteps; ++st) {
     wait_vmcnt<0>();  // step st + 1 landed
     block_sync_lds();
@@ -595,7 +605,8 @@ partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                     const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
                     const uint8_t* __restrict__ kv, const int32_t* __restrict__ bt,
                     int64_t bt_stride, const int32_t* __restrict__ kv_lens,
-                    const int32_t* __restrict__ q_lens, float scale_log2_arg,
+                    const int32_t* __restrict__ q_lens,
+                    const int32_t* __restrict__ kv_bounds, float scale_log2_arg,
                     float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   __shared__ WSmem<NT> sm;
   const PlanDev& P = kDev ? *pdev : Parg;
@@ -629,13 +640,11 @@ partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.part = (int)P.part_base[b] + s;
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
-  const int chunk_tok = chunk_pages_of(P, b) * kPage;
-  const int t0 = s * chunk_tok;
-  it.t1 = max(t0, min(t0 + chunk_tok, it.L));
+  split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
-  it.p_first = t0 / kPage;
+  it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
-  it.nsteps = it.t1 > t0 ? (it.p_end - it.p_first + kStepPages - 1) / kStepPages : 0;
+  it.nsteps = it.t1 > it.t0 ? (it.p_end - it.p_first + kStepPages - 1) / kStepPages : 0;
 
   if (it.w < WRoles<NT>::kQKW) wide_qk<NT>(it, sm);
   else wide_pv<NT>(it, sm);
@@ -646,7 +655,8 @@ partial_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
                         const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
                         float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                        const DeviceArgs* dev, const int32_t* q_lens) {
+                        const DeviceArgs* dev, const int32_t* q_lens,
+                        const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
   const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
@@ -657,17 +667,17 @@ int launch_partial_wide(const mla_decode_plan_s& plan, const uint8_t* q, const u
   if (P.nt == 4) {
     if (dev)
       hipLaunchKernelGGL((partial_wide_kernel<4, true>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
       hipLaunchKernelGGL((partial_wide_kernel<4, false>), grid, dim3(WRoles<4>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   } else {
     if (dev)
       hipLaunchKernelGGL((partial_wide_kernel<6, true>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
     else
       hipLaunchKernelGGL((partial_wide_kernel<6, false>), grid, dim3(WRoles<6>::kThreads), 0, st, P, pd, sd,
-                         q, kv, bt, bt_stride, kv_lens, q_lens, scale_log2, ws_o, ws_stats);
+                         q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
   }
   return (int)hipGetLastError();
 }

@@ -33,6 +33,7 @@ EXPORTS = [
     "mla_decode_partial",
     "mla_decode_merge", "mla_decode_merge_f32", "mla_decode", "mla_decode_varq",
     "mla_decode_graph", "mla_decode_merge_ex", "mla_decode_ex", "mla_decode_graph_ex",
+    "mla_decode_partial_ex", "mla_decode_bounded", "mla_decode_graph_bounded",
     "mla_decode_noalloc", "mla_decode_strerror",
 ]
 
@@ -94,6 +95,14 @@ _lib.mla_decode_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _f32, _f32, _p, _p,
 _lib.mla_decode_graph_ex.restype = ctypes.c_int
 _lib.mla_decode_graph_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p, _p,
                                      _p, _p, _p]
+_lib.mla_decode_partial_ex.restype = ctypes.c_int
+_lib.mla_decode_partial_ex.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _f32, _p, _sz, _p]
+_lib.mla_decode_bounded.restype = ctypes.c_int
+_lib.mla_decode_bounded.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _f32, _f32, _p, _p, _sz,
+                                    _p, _p, _p, _p, _p]
+_lib.mla_decode_graph_bounded.restype = ctypes.c_int
+_lib.mla_decode_graph_bounded.argtypes = [_p, _p, _p, _p, _i64, _p, _p, _p, _p, _p, _p, _p, _sz,
+                                          _p, _p, _p, _p, _p]
 _lib.mla_decode_noalloc.restype = ctypes.c_int
 _lib.mla_decode_noalloc.argtypes = [_p, _p, _p, _p, _i64, _p, _f32, _f32, _p, _p, _p]
 _lib.mla_decode_strerror.restype = ctypes.c_char_p
@@ -261,6 +270,62 @@ def decode(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float,
                            block_table.stride(0), _ptr(kv_lens), float(softmax_scale),
                            float(output_scale), _ptr(workspace), workspace.numel(), _ptr(o),
                            _ptr(lse), _stream(stream)), "mla_decode")
+
+
+def _check_i32(name, t, numel=None):
+    if t is None:
+        return
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 device tensor")
+    if numel is not None and t.numel() != numel:
+        raise TypeError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+def partial_ex(plan: Plan, q, kv_cache, block_table, kv_lens, softmax_scale: float, workspace,
+               q_lens=None, kv_bounds=None, stream=None):
+    """Partial pass with optional q_lens (int32 [B]) and kv_bounds (int32 [B, 2])."""
+    _check_kv(plan, q, kv_cache)
+    _check_i32("q_lens", q_lens, plan.batch)
+    _check_i32("kv_bounds", kv_bounds, 2 * plan.batch)
+    _check(_lib.mla_decode_partial_ex(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                      block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                      _ptr(kv_bounds), float(softmax_scale), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)), "mla_decode_partial_ex")
+
+
+def decode_bounded(plan: Plan, q, kv_cache, block_table, kv_lens, kv_bounds, softmax_scale: float,
+                   output_scale: float, workspace, o=None, lse=None, q_lens=None, sinks=None,
+                   o_fp8=None, o_fp8_scales=None, stream=None):
+    """decode_ex confined to per-request key windows kv_bounds (int32 [B, 2], device)."""
+    _check_kv(plan, q, kv_cache)
+    _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
+    _check_i32("q_lens", q_lens, plan.batch)
+    _check_i32("kv_bounds", kv_bounds, 2 * plan.batch)
+    _check(_lib.mla_decode_bounded(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                   block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                   _ptr(kv_bounds), float(softmax_scale), float(output_scale),
+                                   _ptr(sinks), _ptr(workspace), workspace.numel(), _ptr(o),
+                                   _ptr(lse), _ptr(o_fp8), _ptr(o_fp8_scales), _stream(stream)),
+           "mla_decode_bounded")
+
+
+def decode_graph_bounded(plan: Plan, q, kv_cache, block_table, kv_lens, kv_bounds, softmax_scale,
+                         output_scale, workspace, o=None, lse=None, q_lens=None, sinks=None,
+                         o_fp8=None, o_fp8_scales=None, stream=None):
+    """decode_graph_ex confined to per-request key windows kv_bounds (int32 [B, 2])."""
+    _check_kv(plan, q, kv_cache)
+    _epilogue_args(o, sinks, o_fp8, o_fp8_scales)
+    _check_i32("q_lens", q_lens, plan.batch)
+    _check_i32("kv_bounds", kv_bounds, 2 * plan.batch)
+    for name, t in (("softmax_scale", softmax_scale), ("output_scale", output_scale)):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 device tensor")
+    _check(_lib.mla_decode_graph_bounded(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                         block_table.stride(0), _ptr(kv_lens), _ptr(q_lens),
+                                         _ptr(kv_bounds), _ptr(softmax_scale), _ptr(output_scale),
+                                         _ptr(sinks), _ptr(workspace), workspace.numel(), _ptr(o),
+                                         _ptr(lse), _ptr(o_fp8), _ptr(o_fp8_scales),
+                                         _stream(stream)), "mla_decode_graph_bounded")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20

@@ -286,6 +286,46 @@ int mla_decode_graph_ex(const mla_decode_plan_t* plan, const void* q, const void
                         void* o_fp8_scales, void* stream);
 
 /*
+ * Key windows (kv_bounds, one of the run() arguments that issue #20510, Repro 1, lists
+ * as added after #19338; the pages give it no description). Read here as one half-open
+ * window of key positions per request that its queries are confined to, on top of the
+ * causal rule:
+ *   kv_bounds  device int32 [B][2] = (start_b, end_b): query j of request b sees the keys
+ *              i with start_b <= i < end_b and i <= L_b - q_len_b + j. A negative start
+ *              counts as 0, an end past L_b as L_b. Keys outside the window are never
+ *              read: block-table entries of pages wholly outside it may hold anything,
+ *              and cache slots of the window's first and last page outside it may hold
+ *              anything, NaN codes included.
+ *   A row with no visible key gives O = 0 and LSE = -inf (LSE = sigma_h with a sink).
+ * Splits are planned from the lengths as without windows; a split wholly outside its
+ * request's window does no work. The windows are read on the device at run time.
+ *
+ * mla_decode_partial_ex: mla_decode_partial with optional q_lens (as mla_decode_varq)
+ * and kv_bounds (either may be NULL); merge its partials with any merge call.
+ * mla_decode_bounded: mla_decode_ex with kv_bounds (not NULL).
+ * mla_decode_graph_bounded: mla_decode_graph_ex with kv_bounds (not NULL).
+ */
+int mla_decode_partial_ex(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                          const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                          const int32_t* q_lens, const int32_t* kv_bounds, float softmax_scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+int mla_decode_bounded(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                       const int32_t* block_table, int64_t bt_stride, const int32_t* kv_lens,
+                       const int32_t* q_lens, const int32_t* kv_bounds, float softmax_scale,
+                       float output_scale, const float* sinks, void* workspace,
+                       size_t workspace_bytes, void* o, float* lse, void* o_fp8,
+                       void* o_fp8_scales, void* stream);
+
+int mla_decode_graph_bounded(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
+                             const int32_t* block_table, int64_t bt_stride,
+                             const int32_t* kv_lens, const int32_t* q_lens,
+                             const int32_t* kv_bounds, const float* softmax_scale,
+                             const float* output_scale, const float* sinks, void* workspace,
+                             size_t workspace_bytes, void* o, float* lse, void* o_fp8,
+                             void* o_fp8_scales, void* stream);
+
+/*
  * For callers that cannot allocate device memory or hand in a workspace: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * computation, checks and kernels as mla_decode with a host plan, except that the

@@ -417,3 +417,52 @@ def test_merge_bound_copies(lens, q, h, split):
                        num_cus=256)
     gi = g.info()[0]
     assert g.with_merge_bound(2).info()[0].merge_groups == min(2, gi.merge_groups)
+
+
+def test_bounded_calls_validate_before_launch():
+    """The key-window entry points reject bad arguments on the host (no launch)."""
+    lib = mla.lib_handle()
+    h = plan([100, 50], 1, 12, 2)
+    g = gplan(2, 100)
+    fake = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10002)
+    nul = None
+    need = h.workspace_size()
+    # kv_bounds is required by the bounded calls, and must be 4-byte aligned
+    assert lib.mla_decode_bounded(h.handle, fake, fake, fake, 4, fake, nul, nul, 0.07, 1.0, nul,
+                                  fake, need, fake, nul, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_bounded(h.handle, fake, fake, fake, 4, fake, nul, odd, 0.07, 1.0, nul,
+                                  fake, need, fake, nul, nul, nul, nul) == mla.MLA_ERR_INVALID_ARG
+    # workspace and plan kind checks as for the unbounded calls
+    assert lib.mla_decode_bounded(h.handle, fake, fake, fake, 4, fake, nul, fake, 0.07, 1.0, nul,
+                                  fake, need - 1, fake, nul, nul, nul, nul) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_decode_bounded(g.handle, fake, fake, fake, 4, fake, nul, fake, 0.07, 1.0, nul,
+                                  fake, g.workspace_size(), fake, nul, nul, nul,
+                                  nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph_bounded(h.handle, fake, fake, fake, 4, fake, nul, fake, fake, fake,
+                                        nul, fake, need, fake, nul, nul, nul,
+                                        nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_graph_bounded(g.handle, fake, fake, fake, 4, fake, nul, nul, fake, fake,
+                                        nul, fake, g.workspace_size(), fake, nul, nul, nul,
+                                        nul) == mla.MLA_ERR_INVALID_ARG
+    # the partial pass: windows optional but aligned; short block-table rows refused
+    assert lib.mla_decode_partial_ex(h.handle, fake, fake, fake, 4, fake, nul, odd, 0.07, fake,
+                                     need, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_partial_ex(h.handle, fake, fake, fake, 3, fake, nul, fake, 0.07, fake,
+                                     need, nul) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_partial_ex(g.handle, fake, fake, fake, 4, fake, nul, fake, 0.07, fake,
+                                     need, nul) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_noalloc_validates_before_launch():
+    lib = mla.lib_handle()
+    fake = ctypes.c_void_p(0x10000)
+    g = gplan(2, 100)
+    assert lib.mla_decode_noalloc(None, fake, fake, fake, 4, fake, 0.07, 1.0, fake, None,
+                                  None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_noalloc(g.handle, fake, fake, fake, 4, fake, 0.07, 1.0, fake, None,
+                                  None) == mla.MLA_ERR_INVALID_ARG
+    big = plan([1 << 20] * 4, 8, 128, 1024, cap=1024)
+    assert big.workspace_size() > mla.NOALLOC_SCRATCH_BYTES
+    assert lib.mla_decode_noalloc(big.handle, fake, fake, fake, 32768, fake, 0.07, 1.0, fake, None,
+                                  None) == mla.MLA_ERR_WORKSPACE
