@@ -162,7 +162,20 @@ def test_split_invariance_f32(mla, lens, heads, q_len):
         assert dl <= 1e-5 * max(1.0, float(np.abs(base[2]).max())), (sk, dl)
 
 
-@pytest.mark.parametrize("heads,q_len", [(12, 8), (12, 4), (16, 4), (12, 1)])
+@pytest.mark.parametrize("heads,q_len", [(12, 8), (16, 4), (96, 8), (12, 1)])
+def test_large_score_range(mla, heads, q_len):
+    """Scores spread over hundreds of log2 units (softmax_scale 4): within a split the
+    running maximum jumps by far more than 2^64 between pages, and the weights of most
+    earlier pages underflow to zero once rescaled."""
+    case = inputs.make_case([5000, 700], num_heads=heads, q_len=q_len, seed=31, split_kv=2,
+                            softmax_scale=4.0)
+    _say(f"[gpu] large score range H={heads} q={q_len}")
+    o, lse, _ = run_gpu(mla, case)
+    o_ref, lse_ref = run_oracle(case)
+    assert_parity(o, lse, o_ref, lse_ref, "large range")
+
+
+@pytest.mark.parametrize("heads,q_len", [(12, 8), (12, 4), (16, 4), (12, 1), (96, 8)])
 def test_determinism(mla, heads, q_len):
     """Repeated calls give the same bits (wide blocks of 6 and 4 row tiles, narrow)."""
     case = inputs.make_case([4096, 777], num_heads=heads, q_len=q_len, seed=9, split_kv=3)
