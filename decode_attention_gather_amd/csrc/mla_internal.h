@@ -98,6 +98,13 @@ struct mla_decode_plan_s {
 
 namespace mla {
 
+// A grid of fewer work items than CUs (graph plans: by capacity). Such grids leave
+// CUs idle, and each busy CU must pull more bytes per second: kernels keep more loads
+// in flight per workgroup there.
+inline bool narrow_underfilled(const mla_decode_plan_s& plan) {
+  return (int64_t)plan.dev.total_parts * plan.dev.tiles < (int64_t)plan.num_cus;
+}
+
 // Workspace carve-up: partial O at offset 0, stats after it (256-byte aligned).
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

@@ -141,8 +141,12 @@ struct Item {
 constexpr int kNoKey = -0x40000000;  // causal limit of a row that sees no key
 
 // One wave's whole life: prologue, then 1 + nsteps barriers like every other wave.
-template <int NT, bool kDoQK, bool kDoLd, bool kDoPV>
+// kNB: steps of page data each loader holds in registers (loads in flight per loader):
+// 2 when the grid fills the chip, 3 for grids of fewer work items than CUs, where each
+// CU must pull more bytes per second and only the latency of HBM limits it.
+template <int NT, int kNB, bool kDoQK, bool kDoLd, bool kDoPV>
 __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
+  static_assert(kNB == 2 || kNB == 3, "loader buffers (the tail below runs < 3 steps)");
   using R = Roles<NT>;
   const PlanDev& P = *it.P;
   const int lane = it.lane, w = it.w, g = it.g, l16 = it.l16;
@@ -398,53 +402,53 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   };
 
   // ---------------- pipeline ----------------
-  // The data of step t is loaded at iteration t - 4 (steps 0-3 before the loop) and
-  // stored to LDS at iteration t - 2; loader buffers alternate by step parity (A even,
-  // B odd). QK of step t runs in iteration t - 1 (step 0 before the loop), PV of step t
-  // in iteration t. The loader's loads are unconditional and the loop runs over pairs
-  // of steps, so each store waits for exactly one buffer while the other stays in
-  // flight.
-  v4i bufA[kLd], bufB[kLd];
+  // The data of step t is loaded into loader buffer t % kNB at iteration t - 2 - kNB
+  // (steps 0 .. kNB + 1 before the loop) and stored to LDS at iteration t - 2, which
+  // then loads step t + kNB into the same buffer. QK of step t runs in iteration t - 1
+  // (step 0 before the loop), PV of step t in iteration t. The loop body covers kNB
+  // steps, so buffer indices are constants; each store waits for its own buffer, the
+  // oldest in flight, while the other kNB - 1 stay in flight. The loads are
+  // unconditional (steps past the split's end repeat its last page, never read). The
+  // last nsteps % kNB (< 3) steps store nothing: their stages were stored by then.
+  v4i buf[kNB][kLd];
   int64_t nid_a = 0, nid_b = 0;
   if (kDoLd && nsteps > 0) {
     int64_t ia, ib;
-    page_ids(0, &ia, &ib);
-    gload(ia, ib, bufA);
-    page_ids(1, &ia, &ib);
-    gload(ia, ib, bufB);
-    lstore(0, bufA);
-    page_ids(2, &ia, &ib);
-    gload(ia, ib, bufA);
-    lstore(1, bufB);
-    page_ids(3, &ia, &ib);
-    gload(ia, ib, bufB);
-    page_ids(4, &nid_a, &nid_b);
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      page_ids(j, &ia, &ib);
+      gload(ia, ib, buf[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lstore(j, buf[j]);
+      page_ids(kNB + j, &ia, &ib);
+      gload(ia, ib, buf[j]);
+    }
+    page_ids(kNB + 2, &nid_a, &nid_b);
   }
   block_sync_lds();  // steps 0 and 1 stored
   if (kDoQK && nsteps > 0) qk_step(0);
-  const int npairs = nsteps >> 1;
-  for (int i = 0; i < npairs; ++i) {
-    const int st = 2 * i;
-    block_sync_lds();  // stage st + 1 stored, P~(st) ready, PV(st - 1) done everywhere
-    if (kDoLd) {
-      lstore(st + 2, bufA);
-      gload(nid_a, nid_b, bufA);
-      page_ids(st + 5, &nid_a, &nid_b);
+  const int ngroups = nsteps / kNB;
+  for (int i = 0; i < ngroups; ++i) {
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      const int st = kNB * i + j;
+      block_sync_lds();  // stage st + 1 stored, P~(st) ready, PV(st - 1) done everywhere
+      if (kDoLd) {
+        lstore(st + 2, buf[(j + 2) % kNB]);
+        gload(nid_a, nid_b, buf[(j + 2) % kNB]);
+        page_ids(st + 3 + kNB, &nid_a, &nid_b);
+      }
+      // st + 1 < nsteps holds inside a group but for its last step
+      if (kDoQK && (j + 1 < kNB || st + 1 < nsteps)) qk_step(st + 1);
+      if (kDoPV) pv_step(st);
     }
-    if (kDoQK) qk_step(st + 1);
-    if (kDoPV) pv_step(st);
-    block_sync_lds();
-    if (kDoLd) {
-      lstore(st + 3, bufB);
-      gload(nid_a, nid_b, bufB);
-      page_ids(st + 6, &nid_a, &nid_b);
-    }
-    if (kDoQK && st + 2 < nsteps) qk_step(st + 2);
-    if (kDoPV) pv_step(st + 1);
   }
-  if (nsteps & 1) {
+  for (int st = kNB * ngroups; st < nsteps; ++st) {
     block_sync_lds();
-    if (kDoPV) pv_step(nsteps - 1);
+    if (kDoQK && st + 1 < nsteps) qk_step(st + 1);
+    if (kDoPV) pv_step(st);
   }
 
   // ---------------- write the partials ----------------
@@ -469,7 +473,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
 }
 
 // kDev: the plan and the softmax scale come from device memory (graph path).
-template <int NT, bool kDev>
+template <int NT, int kNB, bool kDev>
 __global__ void __launch_bounds__(Roles<NT>::kThreads, 1)
 partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
@@ -517,9 +521,9 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
   const int w = it.w;
   using R = Roles<NT>;
-  if (w < R::kQK) wave_main<NT, true, false, false>(it, sm);
-  else if (w < R::kPVFirst) wave_main<NT, false, true, false>(it, sm);
-  else wave_main<NT, false, false, true>(it, sm);
+  if (w < R::kQK) wave_main<NT, kNB, true, false, false>(it, sm);
+  else if (w < R::kPVFirst) wave_main<NT, kNB, false, true, false>(it, sm);
+  else wave_main<NT, kNB, false, false, true>(it, sm);
 }
 
 }  // namespace
@@ -544,17 +548,20 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   const PlanDev* pd = dev ? dev->plan : nullptr;
   const float* sd = dev ? dev->softmax_scale : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  if (P.nt == 1) {
-    if (dev)
-      hipLaunchKernelGGL((partial_kernel<1, true>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
-    else
-      hipLaunchKernelGGL((partial_kernel<1, false>), grid, dim3(Roles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
+#define MLA_NARROW_LAUNCH(NT, NB, DEV)                                                       \
+  hipLaunchKernelGGL((partial_kernel<NT, NB, DEV>), grid, dim3(Roles<NT>::kThreads), 0, st, P, \
+                     pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2,    \
+                     ws_o, ws_stats)
+  // one row tile and fewer work items than CUs: three steps of loads in flight per
+  // loader (the two-tile kernel has no registers to spare for a third buffer)
+  if (P.nt == 1 && narrow_underfilled(plan)) {
+    if (dev) MLA_NARROW_LAUNCH(1, 3, true); else MLA_NARROW_LAUNCH(1, 3, false);
+  } else if (P.nt == 1) {
+    if (dev) MLA_NARROW_LAUNCH(1, 2, true); else MLA_NARROW_LAUNCH(1, 2, false);
   } else {
-    if (dev)
-      hipLaunchKernelGGL((partial_kernel<2, true>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
-    else
-      hipLaunchKernelGGL((partial_kernel<2, false>), grid, dim3(Roles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
+    if (dev) MLA_NARROW_LAUNCH(2, 2, true); else MLA_NARROW_LAUNCH(2, 2, false);
   }
+#undef MLA_NARROW_LAUNCH
   return (int)hipGetLastError();
 }
 

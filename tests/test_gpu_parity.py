@@ -187,6 +187,34 @@ def test_determinism(mla, heads, q_len):
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("lens,split,bounded", [
+    ([1, 100, 2049], 3, False),          # ragged, steps % 3 of 0, 1 and 2
+    ([5000], 1, False),
+    ([3 * 32 + 7, 5 * 32, 33], 2, True),  # key windows inside pages
+    ([131072], 6, False),
+])
+def test_loader_depth_same_bits(mla, lens, split, bounded):
+    """The one-tile kernel keeps three steps of loads in flight per loader when the grid
+    has fewer work items than CUs, two otherwise: the partials (workspace) must be the
+    same bits either way. num_cus 1 makes every grid full."""
+    case = inputs.make_case(lens, num_heads=12, q_len=1, seed=41, split_kv=split)
+    dc = mla.to_device(case)
+    kvb = None
+    if bounded:
+        kvb = torch.tensor([[min(5, n), n] for n in lens], dtype=torch.int32, device="cuda")
+    _say(f"[gpu] loader depth lens={lens} split={split} bounded={bounded}")
+    ws = []
+    for cus in (256, 1):
+        plan = mla.Plan(dc.kv_lens_host, q_len=1, num_heads=12, split_kv=split, num_cus=cus)
+        w = torch.zeros(plan.workspace_size(), dtype=torch.uint8, device="cuda")
+        mla.partial_ex(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, case.softmax_scale, w,
+                       kv_bounds=kvb)
+        torch.cuda.synchronize()
+        ws.append(w.cpu().numpy())
+    assert ws[0].shape == ws[1].shape
+    assert np.array_equal(ws[0], ws[1])
+
+
 def test_device_lengths_shorter_than_plan(mla):
     """A device kv_len below the planned one leaves trailing splits empty; the result is
     the one for the shorter length."""
