@@ -201,6 +201,17 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     return MLA_ERR_UNSUPPORTED_SHAPE;
   }
   d.total_parts = (int32_t)total;
+  // A split plan that leaves CUs idle with 96-row blocks (a fixed split_kv) takes blocks
+  // of 64 rows instead when the larger grid still fits one wave of the chip: a work
+  // item then costs about two thirds as much, and the extra reads of each page come
+  // from idle CUs' share of HBM. A row's arithmetic does not depend on its block.
+  if (nt == kWideMaxTiles) {
+    const int32_t tiles4 = (int32_t)ceil_div(ceil_div(rows, kTileRows), 4);
+    if (total <= split_budget(num_cus, tiles4)) {
+      d.nt = 4;
+      d.tiles = tiles = tiles4;
+    }
+  }
 
   // Longest request first, so the longest work items start in the first wave.
   std::vector<int32_t> order(batch);

@@ -48,19 +48,30 @@ def test_uniform_and_short_plans(lens, q, h, split, exp_splits, exp_chunk):
     info, splits, chunk = p.info()
     assert splits == exp_splits and chunk == exp_chunk
     assert info.rows_per_request == q * h
-    assert info.row_tiles == expected_row_blocks(q * h)
+    assert info.row_tiles == expected_row_blocks(q * h, sum(splits))
     assert info.total_splits == sum(splits)
     assert info.work_items == sum(splits) * info.row_tiles
 
 
-def expected_row_blocks(rows):
+def split_budget(cus, tiles):
+    per_xcd = (cus // 8) // tiles
+    return per_xcd * 8 if per_xcd >= 1 else max(1, cus // tiles)
+
+
+def expected_row_blocks(rows, total_splits=None, cus=256):
     """Row blocks of 16-row tiles: one block of <= 2 tiles up to 32 rows, otherwise as
-    few blocks of <= 6 tiles as cover the rows, each rounded up to 4 or 6 tiles."""
+    few blocks of <= 6 tiles as cover the rows, each rounded up to 4 or 6 tiles. A plan
+    whose splits leave CUs idle takes blocks of 4 tiles instead of 6 when the larger
+    grid still fits one wave of the chip (total_splits given)."""
     tiles16 = math.ceil(rows / 16)
     if tiles16 <= 2:
         return 1
     blocks = math.ceil(tiles16 / 6)
     nt = 4 if math.ceil(tiles16 / blocks) <= 4 else 6
+    if nt == 6 and total_splits is not None:
+        tiles4 = math.ceil(tiles16 / 4)
+        if total_splits <= split_budget(cus, tiles4):
+            return tiles4
     return math.ceil(tiles16 / nt)
 
 
@@ -68,9 +79,23 @@ def expected_row_blocks(rows):
                                           (65, 1), (96, 1), (97, 2), (128, 2), (192, 2),
                                           (768, 8), (4096, 43)])
 def test_row_blocks(rows, blocks):
+    """The minimal blocking, on a plan that fills the chip (cus = 2 leaves no idle CU)."""
     assert expected_row_blocks(rows) == blocks
-    info, _, _ = plan([4096], 1, rows, 2).info()
+    info, _, _ = plan([4096], 1, rows, 2, cus=2).info()
     assert info.row_tiles == blocks
+
+
+@pytest.mark.parametrize("lens,q,h,split,cus,tiles", [
+    ([131072] * 16, 8, 12, 6, 256, 2),   # 96 splits of 96 rows: 192 blocks of 64 rows
+    ([131072] * 16, 8, 12, 0, 256, 1),   # the planner fills the chip with 96-row blocks
+    ([131072] * 16, 8, 12, 6, 128, 1),   # 192 items would not fit 128 CUs
+    ([4096] * 8, 8, 96, 2, 256, 12),     # H96: 16 splits x 12 blocks of 64 rows
+    ([4096] * 8, 8, 96, 4, 256, 8),      # 32 splits x 12 blocks would not fit one wave
+])
+def test_underfilled_plans_take_64_row_blocks(lens, q, h, split, cus, tiles):
+    info, splits, _ = plan(lens, q, h, split, cus=cus).info()
+    assert info.row_tiles == tiles == expected_row_blocks(q * h, sum(splits), cus)
+    assert info.work_items == sum(splits) * tiles
 
 
 def check_cover(lens, splits, chunk):
@@ -341,12 +366,18 @@ def test_epilogue_validation_before_launch():
 ])
 def test_bf16_plans_share_the_row_block_rule(rows_q, heads, exp_tiles):
     """BF16 plans block rows as E4M3 plans do: up to 32 rows in one block, more in as
-    few blocks of at most 96 rows as cover them."""
-    p = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=256,
-                 kv_dtype="bf16")
-    info = p.info()[0]
-    assert info.row_tiles == exp_tiles
-    assert info.work_items == info.total_splits * exp_tiles
+    few blocks of at most 96 rows as cover them (graph plans; and host plans that fill
+    the chip), and 64-row blocks where a host plan leaves CUs idle."""
+    for cus in (256, 2):
+        p = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=cus,
+                     kv_dtype="bf16")
+        e = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=cus)
+        info = p.info()[0]
+        assert info.row_tiles == e.info()[0].row_tiles
+        assert info.row_tiles == expected_row_blocks(rows_q * heads, info.total_splits, cus)
+        assert info.work_items == info.total_splits * info.row_tiles
+        if cus == 2:
+            assert info.row_tiles == exp_tiles
     g = mla.Plan.graph(2, q_len=rows_q, num_heads=heads, max_kv_len=4096, num_cus=256,
                        kv_dtype="bf16")
     assert g.info()[0].row_tiles == exp_tiles

@@ -41,10 +41,22 @@ def test_max_rows_per_request(mla):
     _say("[gpu] limits: 4096 rows per request (H 128, q 32)")
     o, lse, plan = run_gpu(mla, case, split_kv=2)
     info = plan.info()[0]
-    assert info.rows_per_request == 4096 and info.row_tiles == 43
+    # 4 splits leave CUs idle: 64 blocks of 64 rows
+    assert info.rows_per_request == 4096 and info.row_tiles == 64
     rows = inputs.sample_rows(case, 600, seed=5)
     o_ref, lse_ref = run_oracle(case, rows)
     assert_parity(o[rows], lse[rows], o_ref, lse_ref, "4096 rows")
+    # planned for 8 CUs the same splits fill the chip: 43 blocks of 96 rows, the last
+    # one of 64 rows and 32 padding rows; a row's bits do not depend on its block
+    _say("[gpu] limits: 4096 rows in 96-row blocks")
+    dc = mla.to_device(case)
+    p96 = mla.Plan(dc.kv_lens_host, q_len=32, num_heads=128, split_kv=2, num_cus=8)
+    assert p96.info()[0].row_tiles == 43
+    assert p96.info()[0].merge_groups == info.merge_groups  # the same merge order
+    o96, lse96 = mla.run_decode(dc, p96)
+    torch.cuda.synchronize()
+    assert np.array_equal(o96.float().cpu().numpy(), o)
+    assert np.array_equal(lse96.cpu().numpy(), lse)
 
 
 def test_split_longer_than_chunk_limit(mla):
