@@ -84,6 +84,25 @@ struct Roles {
   static constexpr int kDimSlices = 32 / kDimTiles;                // 4 PV waves per row tile
   static_assert(kDimSlices * NT == kWaves - kPVFirst, "PV waves cover every (row tile, dim slice)");
   static constexpr int kMaxLd = kChunksPerStep / kLdWaves;    // 9
+  // Waves w, w + 4, w + 8 share a SIMD (a workgroup's waves are dealt round-robin).
+  // NT = 2: QK 0-3, loaders 4-7, PV 8-15, the same mix on every SIMD. NT = 1: QK 0-1,
+  // PV 2-3 and 6-7, loaders 4-5 and 8-9, so that the two SIMDs that run a QK wave get
+  // two loaders beside it (the lightest role) and the other two a pair of PV waves;
+  // QK, loaders and PV 0-5 in that order left the QK SIMDs with a loader and a PV wave
+  // each and the others with a loader and a PV wave half idle.
+  enum { kRoleQK, kRoleLd, kRolePV };
+  static __device__ __forceinline__ int role(int w) {
+    if (w < kQK) return kRoleQK;
+    if (NT == 2) return w < kPVFirst ? kRoleLd : kRolePV;
+    return (w & 3) >= 2 && w < 8 ? kRolePV : kRoleLd;
+  }
+  // index among the loaders (0 .. kLdWaves - 1) and among the PV waves
+  static __device__ __forceinline__ int ld_index(int w) {
+    return NT == 2 ? w - kLdFirst : (w < 8 ? w - 4 : w - 6);
+  }
+  static __device__ __forceinline__ int pv_index(int w) {
+    return NT == 2 ? w - kPVFirst : (w < 6 ? w - 2 : w - 4);
+  }
 };
 
 template <int NT>
@@ -259,7 +278,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
 
   // ---------------- loader role ----------------
   static_assert(kChunksPerStep % R::kLdWaves == 0, "every loader issues the same loads");
-  const int li = w - R::kLdFirst;
+  const int li = R::ld_index(w);
   constexpr int kLd = kDoLd ? R::kMaxLd : 1;
   // Loader li owns the kLd consecutive 1 KB chunks k = li kLd .. li kLd + kLd - 1 of a
   // step (chunk k = byte 1024 (k % 18) of page k / 18), all within one page, so each
@@ -295,7 +314,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   };
 
   // ---------------- PV role ----------------
-  const int pv_w = w - R::kPVFirst;
+  const int pv_w = R::pv_index(w);
   const int pv_rt = pv_w / R::kDimSlices;  // row tile of the wave
   const int pv_ds = pv_w % R::kDimSlices;  // dims [16 kDimTiles pv_ds, ...)
   const bool pv_own = pv_ds == 0;          // the wave that keeps l and l~ of its row tile
@@ -521,8 +540,9 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
   const int w = it.w;
   using R = Roles<NT>;
-  if (w < R::kQK) wave_main<NT, kNB, true, false, false>(it, sm);
-  else if (w < R::kPVFirst) wave_main<NT, kNB, false, true, false>(it, sm);
+  const int role = R::role(w);
+  if (role == R::kRoleQK) wave_main<NT, kNB, true, false, false>(it, sm);
+  else if (role == R::kRoleLd) wave_main<NT, kNB, false, true, false>(it, sm);
   else wave_main<NT, kNB, false, false, true>(it, sm);
 }
 
