@@ -75,6 +75,26 @@ struct BRoles {
   static constexpr int kDimTiles = 32 / (kWaves - kPVFirst);  // 8 or 4
   static constexpr int kMaxLd = kChunks / kLdWaves;          // 9
   static_assert(kMaxLd * kLdWaves == kChunks, "every loader issues the same loads");
+  // Waves w, w + 4, w + 8 share a SIMD. In order (QK, loaders, PV), one tile puts a
+  // QK, a loader and a PV wave on SIMDs 0-1 and a loader and a PV wave on 2-3. kSpread
+  // (one tile, grids of fewer work items than CUs): QK 0-1, PV 2-3 and 6-7, loaders 4-5
+  // and 8-9, so the QK SIMDs get two loaders beside the QK wave and the other two a PV
+  // pair (split 6: 754 -> 660 us; on grids that fill the chip it cost 1%).
+  enum { kRoleQK, kRoleLd, kRolePV };
+  template <bool kSpread>
+  static __device__ __forceinline__ int role(int w) {
+    if (w < kQK) return kRoleQK;
+    if (!kSpread) return w < kPVFirst ? kRoleLd : kRolePV;
+    return (w & 3) >= 2 && w < 8 ? kRolePV : kRoleLd;
+  }
+  template <bool kSpread>
+  static __device__ __forceinline__ int ld_index(int w) {
+    return !kSpread ? w - kLdFirst : (w < 8 ? w - 4 : w - 6);
+  }
+  template <bool kSpread>
+  static __device__ __forceinline__ int pv_index(int w) {
+    return !kSpread ? w - kPVFirst : (w < 6 ? w - 2 : w - 4);
+  }
 };
 
 template <int NT>
@@ -130,8 +150,9 @@ struct BItem {
 
 constexpr int kNoKey = -0x40000000;
 
-template <int NT, bool kDoQK, bool kDoLd, bool kDoPV>
+template <int NT, bool kSpread, bool kDoQK, bool kDoLd, bool kDoPV>
 __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
+  static_assert(!kSpread || NT == 1, "spread placement: one row tile");
   using R = BRoles<NT>;
   const PlanDev& P = *it.P;
   const int lane = it.lane, w = it.w, g = it.g, l16 = it.l16;
@@ -221,7 +242,7 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
   };
 
   // ---------------- loader role ----------------
-  const int li = w - R::kLdFirst;
+  const int li = R::template ld_index<kSpread>(w);
   constexpr int kLd = kDoLd ? R::kMaxLd : 1;
   // Loader li owns the kLd consecutive 1 KB chunks li kLd .. li kLd + kLd - 1 of the
   // step's page; lane i moves 16 bytes into padded LDS row n.
@@ -247,7 +268,7 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
   };
 
   // ---------------- PV role ----------------
-  const int pv_w = w - R::kPVFirst;
+  const int pv_w = R::template pv_index<kSpread>(w);
   constexpr int kDT = kDoPV ? R::kDimTiles : 1;
   constexpr int kNTp = kDoPV ? NT : 1;
   v4f acc[kNTp][kDT];
@@ -403,7 +424,7 @@ __device__ __forceinline__ void bwave_main(const BItem& it, BSmem<NT>& sm) {
   }
 }
 
-template <int NT, bool kDev>
+template <int NT, bool kDev, bool kSpread>
 __global__ void __launch_bounds__(BRoles<NT>::kThreads, 1)
 partial_bf16_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
                     const float* __restrict__ scale_dev, const uint8_t* __restrict__ q,
@@ -451,9 +472,10 @@ partial_bf16_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
   const int w = it.w;
   using R = BRoles<NT>;
-  if (w < R::kQK) bwave_main<NT, true, false, false>(it, sm);
-  else if (w < R::kPVFirst) bwave_main<NT, false, true, false>(it, sm);
-  else bwave_main<NT, false, false, true>(it, sm);
+  const int role = R::template role<kSpread>(w);
+  if (role == R::kRoleQK) bwave_main<NT, kSpread, true, false, false>(it, sm);
+  else if (role == R::kRoleLd) bwave_main<NT, kSpread, false, true, false>(it, sm);
+  else bwave_main<NT, kSpread, false, false, true>(it, sm);
 }
 
 }  // namespace
@@ -469,17 +491,18 @@ int launch_partial_bf16(const mla_decode_plan_s& plan, const uint8_t* q, const u
   const PlanDev* pd = dev ? dev->plan : nullptr;
   const float* sd = dev ? dev->softmax_scale : nullptr;
   hipStream_t st = (hipStream_t)stream;
-  if (P.nt == 1) {
-    if (dev)
-      hipLaunchKernelGGL((partial_bf16_kernel<1, true>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
-    else
-      hipLaunchKernelGGL((partial_bf16_kernel<1, false>), grid, dim3(BRoles<1>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
+#define MLA_BF16_LAUNCH(NT, DEV, SPREAD)                                                    \
+  hipLaunchKernelGGL((partial_bf16_kernel<NT, DEV, SPREAD>), grid, dim3(BRoles<NT>::kThreads), \
+                     0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds,       \
+                     scale_log2, ws_o, ws_stats)
+  if (P.nt == 1 && narrow_underfilled(plan)) {
+    if (dev) MLA_BF16_LAUNCH(1, true, true); else MLA_BF16_LAUNCH(1, false, true);
+  } else if (P.nt == 1) {
+    if (dev) MLA_BF16_LAUNCH(1, true, false); else MLA_BF16_LAUNCH(1, false, false);
   } else {
-    if (dev)
-      hipLaunchKernelGGL((partial_bf16_kernel<2, true>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
-    else
-      hipLaunchKernelGGL((partial_bf16_kernel<2, false>), grid, dim3(BRoles<2>::kThreads), 0, st, P, pd, sd, q, kv, bt, bt_stride, kv_lens, q_lens, kv_bounds, scale_log2, ws_o, ws_stats);
+    if (dev) MLA_BF16_LAUNCH(2, true, false); else MLA_BF16_LAUNCH(2, false, false);
   }
+#undef MLA_BF16_LAUNCH
   return (int)hipGetLastError();
 }
 
