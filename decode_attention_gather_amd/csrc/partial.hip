@@ -317,11 +317,14 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
   const int pv_w = R::pv_index(w);
   const int pv_rt = pv_w / R::kDimSlices;  // row tile of the wave
   const int pv_ds = pv_w % R::kDimSlices;  // dims [16 kDimTiles pv_ds, ...)
-  const bool pv_own = pv_ds == 0;          // the wave that keeps l and l~ of its row tile
+  // the waves that keep l (dim slice 0) and l~ (dim slice 1) of their row tile: two
+  // waves on different SIMDs share the extra work
+  const bool pv_own = pv_ds == 0;
+  const bool pv_own_t = pv_ds == 1;
   constexpr int kDT = kDoPV ? R::kDimTiles : 1;
   constexpr int kNTp = 1;                  // row tiles per PV wave (rt below is 0)
   v4f acc[kNTp][kDT];
-  v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile pv_rt (pv_own): ones product
+  v4f acc1 = v4f{0.f, 0.f, 0.f, 0.f};  // l~ of row tile pv_rt (pv_own_t): ones product
   float m_c[kNTp][4];  // running max of result rows
   float m_a[kNTp];     // running max of operand rows (row l16 of the tile)
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // l of rows 4g + jj of row tile pv_rt (pv_own)
@@ -369,7 +372,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
           acc[rt][d][0] *= alpha[0]; acc[rt][d][1] *= alpha[1];
           acc[rt][d][2] *= alpha[2]; acc[rt][d][3] *= alpha[3];
         }
-        if (pv_own) {
+        if (pv_own_t) {
           acc1[0] *= alpha[0]; acc1[1] *= alpha[1]; acc1[2] *= alpha[2]; acc1[3] *= alpha[3];
         }
       }
@@ -380,7 +383,7 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
       sa[rt] = cp == -INFINITY ? 127 : max(0, 127 + (int)(cp - m_a[rt]) - 4 * (g >> 1));
       const uint8_t* prow = sm.ptile[pb] + ((pv_rt + rt) * kTileRows + l16) * kPRow + 16 * g;
       pa[rt] = cat8(ld16(prow, 0), ld16(prow, 64));
-      if (pv_own) {
+      if (pv_own_t) {
         const v8i ones = v8i{kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
                              kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
         acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pa[rt], ones, acc1, 0, 0, 0, sa[rt], 0, 127);
@@ -483,8 +486,11 @@ __device__ __forceinline__ void wave_main(const Item& it, Smem<NT>& sm) {
 #pragma unroll
           for (int d = 0; d < kDT; ++d) orow[16 * d] = acc[rt][d][jj];
           if (pv_own && l16 == 0)
-            *(float4*)(it.ws_stats + (part_row0 + row) * kStatStride) =
-                make_float4(m_c[rt][jj], lsum[jj], acc1[jj], 0.f);
+            *(float2*)(it.ws_stats + (part_row0 + row) * kStatStride) =
+                make_float2(m_c[rt][jj], lsum[jj]);
+          if (pv_own_t && l16 == 0)
+            *(float2*)(it.ws_stats + (part_row0 + row) * kStatStride + 2) =
+                make_float2(acc1[jj], 0.f);
         }
       }
     }
