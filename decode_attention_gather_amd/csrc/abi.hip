@@ -29,8 +29,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int check_workspace(const mla_decode_plan_s* plan, const void* ws, size_t bytes) {
   if (ws == nullptr || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
-  if (bytes < plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes)
-    return MLA_ERR_WORKSPACE;
+  if (bytes < workspace_bytes_of(*plan)) return MLA_ERR_WORKSPACE;
   return MLA_OK;
 }
 
@@ -180,7 +179,7 @@ int mla_decode_noalloc(const mla_decode_plan_t* plan, const void* q, const void*
                        float softmax_scale, float output_scale, void* o, float* lse,
                        void* stream) {
   if (plan == nullptr || plan->device_lengths) return MLA_ERR_INVALID_ARG;
-  const size_t need = plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes;
+  const size_t need = workspace_bytes_of(*plan);
   if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
   void* ws = nullptr;
   int rc = scratch_of_current_device(&ws);

@@ -246,7 +246,54 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
     lse[row_global] = L > 0.f ? 0.69314718055994531f * ((Mx - 8.f) + log2f(L)) : -INFINITY;
 }
 
+// Fold of cooperative splits (plans whose dev.subs > 1 run a split on several
+// workgroups, each over its own run of the split's keys): the partial state of (split p,
+// row r) from its sub-ranges' states by the combine above without the final division,
+//     M = max_i m_i,  O = sum_i 2^(m_i - M) O_i,  l = sum_i 2^(m_i - M) l_i  (same for l~),
+// in sub-range order. One wavefront per (split, row); lane i owns dims [8 i, 8 i + 8).
+__global__ void __launch_bounds__(256)
+fold_kernel(int n, int rows, int subs, const float* __restrict__ sub_o,
+            const float* __restrict__ sub_stats, float* __restrict__ o,
+            float* __restrict__ stats) {
+  const int w = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (w >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int p = w / rows, r = w - p * rows;
+  const int64_t k0 = (int64_t)p * subs * rows + r;  // slot of (p, sub 0, r); sub i: + i rows
+  float M = -INFINITY;
+  for (int i = 0; i < subs; ++i) M = fmaxf(M, sub_stats[(k0 + (int64_t)i * rows) * kStatStride]);
+  float l = 0.f, lt = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+  for (int i = 0; i < subs; ++i) {
+    const int64_t k = k0 + (int64_t)i * rows;
+    const float4 st = *(const float4*)(sub_stats + k * kStatStride);
+    const float wt = pow2i(st.x, M);
+    if (wt == 0.f) continue;  // a sub-range without a visible key (wave-uniform)
+    l += wt * st.y;
+    lt += wt * st.z;
+    const float4* src = (const float4*)(sub_o + k * kDV + 8 * lane);
+    const float4 x = src[0], y = src[1];
+    a.x += wt * x.x; a.y += wt * x.y; a.z += wt * x.z; a.w += wt * x.w;
+    b.x += wt * y.x; b.y += wt * y.y; b.z += wt * y.z; b.w += wt * y.w;
+  }
+  float4* dst = (float4*)(o + ((int64_t)p * rows + r) * kDV + 8 * lane);
+  dst[0] = a;
+  dst[1] = b;
+  if (lane == 0)
+    *(float4*)(stats + ((int64_t)p * rows + r) * kStatStride) = make_float4(M, l, lt, 0.f);
+}
+
 }  // namespace
+
+int launch_fold(const mla_decode_plan_s& plan, const float* sub_o, const float* sub_stats,
+                float* o, float* stats, void* stream) {
+  const PlanDev& P = plan.dev;
+  const int n = P.total_parts * P.rows;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(fold_kernel, dim3((n + 3) / 4), dim3(256), 0, (hipStream_t)stream, n,
+                     P.rows, P.subs, sub_o, sub_stats, o, stats);
+  return (int)hipGetLastError();
+}
 
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,

@@ -26,6 +26,8 @@ constexpr int kMaxChunkPages = 65535;      // split length limit (fits uint16)
 constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
 constexpr int kMergeWavesPerCu = 32;      // merge launch budget: waves resident per CU
 constexpr int kMaxMergeSlices = 8;         // merge: at most 8 workgroups per row
+constexpr int kMaxSubs = 8;                // workgroups sharing one split (small grids)
+constexpr int kMinSubSteps = 16;           // 2-page steps per workgroup when shared
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroup i runs on XCD i mod 8
 
 // Everything the kernels need from a plan, passed by value as a kernel argument
@@ -43,6 +45,7 @@ struct PlanDev {
   int32_t total_parts;  // sum of splits
   int32_t nt;           // 16-row tiles per row block: 1, 2 (narrow) or 4, 6 (wide)
   int32_t groups;       // merge: wavefront groups per row (<= the launch's groups)
+  int32_t subs;         // workgroups per (split, row block): 1, or more on a small grid
   uint32_t sorted[kMaxBatch];     // (part_end << 8) | request
   uint32_t kv_len[kMaxBatch];     // per request: the plan's (host) length
   uint32_t part_base[kMaxBatch];  // per request: index of its first split
@@ -73,6 +76,38 @@ __host__ __device__ inline void split_keys(const PlanDev& P, int b, int s, int L
   *t1 = hi > lo ? hi : lo;
 }
 
+// Flat workgroup id -> work item (sorted split index ps, sub-range sub, row block blk).
+// The row blocks of one (split, sub) run on one XCD (workgroup i goes to XCD i mod 8)
+// and (split, sub) pairs are dealt round-robin over the XCDs. False past the last item.
+__host__ __device__ inline bool work_item(const PlanDev& P, int wg, int* ps, int* sub,
+                                          int* blk) {
+  const int x = wg & 7, k = wg >> 3;
+  const int slot = k / P.tiles;
+  *blk = k - slot * P.tiles;
+  const int v = slot * 8 + x;
+  *ps = v / P.subs;
+  *sub = v - *ps * P.subs;
+  return v < P.total_parts * P.subs;
+}
+
+// Keys of sub-range sub of a split's keys [*t0, *t1) when P.subs workgroups share the
+// split: the split's pages, counted from its first, cut into P.subs runs of whole
+// 2-page steps (ceil(steps / subs) each; trailing runs may be empty). An empty run is
+// the empty range at the split's end.
+__host__ __device__ inline void sub_keys(const PlanDev& P, int sub, int* t0, int* t1) {
+  if (P.subs <= 1 || *t1 <= *t0) return;
+  const int pf = *t0 / kPage, pe = (*t1 + kPage - 1) / kPage;
+  const int per = ((pe - pf + 1) / 2 + P.subs - 1) / P.subs;  // steps per run
+  const int lo = (pf + 2 * per * sub) * kPage, hi = (pf + 2 * per * (sub + 1)) * kPage;
+  const int a = lo > *t0 ? lo : *t0, b = hi < *t1 ? hi : *t1;
+  if (b > a) {
+    *t0 = a;
+    *t1 = b;
+  } else {
+    *t0 = *t1;
+  }
+}
+
 }  // namespace mla
 
 // Host-side plan object (opaque to callers). A graph plan (device_lengths != 0) holds
@@ -93,20 +128,28 @@ struct mla_decode_plan_s {
   int32_t num_cus;
   size_t ws_o_bytes;      // fp32 partial O region
   size_t ws_stats_bytes;  // fp32 (m, l, l~, 0) region
+  size_t ws_sub_o_bytes;      // dev.subs > 1: the sub-ranges' fp32 O, after the stats
+  size_t ws_sub_stats_bytes;  // dev.subs > 1: their (m, l, l~, 0), after that
   int32_t* kv_lens;       // host copy [batch]
 };
 
 namespace mla {
 
-// A grid of fewer work items than CUs (graph plans: by capacity). Such grids leave
+// A grid of fewer workgroups than CUs (graph plans: by capacity). Such grids leave
 // CUs idle, and each busy CU must pull more bytes per second: kernels keep more loads
 // in flight per workgroup there.
 inline bool narrow_underfilled(const mla_decode_plan_s& plan) {
-  return (int64_t)plan.dev.total_parts * plan.dev.tiles < (int64_t)plan.num_cus;
+  return (int64_t)plan.dev.total_parts * plan.dev.subs * plan.dev.tiles <
+         (int64_t)plan.num_cus;
 }
 
-// Workspace carve-up: partial O at offset 0, stats after it (256-byte aligned).
+// Workspace carve-up (256-byte aligned regions): [device plan (graph plans)] partial O,
+// stats, and with dev.subs > 1 the sub-ranges' O and stats.
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t workspace_bytes_of(const mla_decode_plan_s& plan) {
+  return plan.ws_plan_bytes + plan.ws_o_bytes + plan.ws_stats_bytes + plan.ws_sub_o_bytes +
+         plan.ws_sub_stats_bytes;
+}
 
 // Graph path: where the kernels find the plan and the scales (device memory).
 struct DeviceArgs {
@@ -151,6 +194,10 @@ struct MergeEpilogue {
 int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* ws_stats,
                  float output_scale, void* o, bool o_is_f32, float* lse, void* stream,
                  const DeviceArgs* dev = nullptr, const MergeEpilogue* epi = nullptr);
+// Split partials from their sub-ranges' partial states (dev.subs > 1): reads sub_o /
+// sub_stats ([split][sub][row]), writes o / stats ([split][row]).
+int launch_fold(const mla_decode_plan_s& plan, const float* sub_o, const float* sub_stats,
+                float* o, float* stats, void* stream);
 // Splits that fill the chip once for row blocks of `tiles` (XCD-aware; plan.cpp).
 int64_t split_budget(int32_t num_cus, int32_t tiles);
 int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,

@@ -127,17 +127,6 @@ __device__ __forceinline__ void block_sync_lds() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Map the flat workgroup id to (sorted split index, row block) so that the row blocks
-// of one split run on the same XCD (workgroup i goes to XCD i mod 8) and splits are
-// dealt round-robin over the XCDs.
-__device__ __forceinline__ bool wg_item(const PlanDev& P, int wg, int* part_sorted, int* blk) {
-  const int x = wg & 7, k = wg >> 3;
-  const int slot = k / P.tiles;
-  *blk = k - slot * P.tiles;
-  *part_sorted = slot * 8 + x;
-  return *part_sorted < P.total_parts;
-}
-
 // 2^(a - b) for integer-valued a <= b; 0 when a is -inf.
 __device__ __forceinline__ float pow2_diff(float a, float b) {
   return a == -INFINITY ? 0.f : ldexp_int(1.f, (int)(a - b));
@@ -514,8 +503,8 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   it.g = it.lane >> 4;
   it.l16 = it.lane & 15;
-  int ps, blk;
-  if (!wg_item(P, blockIdx.x, &ps, &blk)) return;
+  int ps, sub, blk;
+  if (!work_item(P, blockIdx.x, &ps, &sub, &blk)) return;
   int e = 0;
   {
     int lo = 0, hi = P.batch - 1;
@@ -535,10 +524,11 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.ws_stats = ws_stats;
   it.scale_log2 = scale_log2;
   it.b = b;
-  it.part = (int)P.part_base[b] + s;
+  it.part = ((int)P.part_base[b] + s) * P.subs + sub;  // subs > 1: the sub-range slot
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
   split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
+  sub_keys(P, sub, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
   it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
@@ -554,10 +544,13 @@ partial_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 
 }  // namespace
 
-int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
-                   const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
-                   float softmax_scale, float* ws_o, float* ws_stats, void* stream,
-                   const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds) {
+namespace {
+
+int launch_partial_kernel(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                          const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                          float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                          const DeviceArgs* dev, const int32_t* q_lens,
+                          const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
   if (plan.kv_dtype == MLA_KV_BF16 && P.nt > kMaxTilesPerBlock)
     return launch_partial_bf16_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o,
@@ -568,7 +561,7 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   if (P.nt > kMaxTilesPerBlock)
     return launch_partial_wide(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o, ws_stats,
                                stream, dev, q_lens, kv_bounds);
-  const int slots = (P.total_parts + 7) / 8;  // graph plans: the capacity
+  const int slots = (P.total_parts * P.subs + 7) / 8;  // graph plans: the capacity
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   const PlanDev* pd = dev ? dev->plan : nullptr;
@@ -589,6 +582,25 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   }
 #undef MLA_NARROW_LAUNCH
   return (int)hipGetLastError();
+}
+
+}  // namespace
+
+// With dev.subs > 1 the kernels write one partial state per (split, sub-range) into the
+// region after the stats, and the fold kernel turns them into the split partials.
+int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_t* kv,
+                   const int32_t* bt, int64_t bt_stride, const int32_t* kv_lens,
+                   float softmax_scale, float* ws_o, float* ws_stats, void* stream,
+                   const DeviceArgs* dev, const int32_t* q_lens, const int32_t* kv_bounds) {
+  if (plan.dev.subs <= 1)
+    return launch_partial_kernel(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale, ws_o,
+                                 ws_stats, stream, dev, q_lens, kv_bounds);
+  float* sub_o = (float*)((uint8_t*)ws_stats + plan.ws_stats_bytes);
+  float* sub_stats = (float*)((uint8_t*)sub_o + plan.ws_sub_o_bytes);
+  const int rc = launch_partial_kernel(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale,
+                                       sub_o, sub_stats, stream, dev, q_lens, kv_bounds);
+  if (rc != 0) return rc;
+  return launch_fold(plan, sub_o, sub_stats, ws_o, ws_stats, stream);
 }
 
 }  // namespace mla

@@ -169,14 +169,6 @@ __device__ __forceinline__ float pow2_diff(float a, float b) {
   return a == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(a - b));
 }
 
-__device__ __forceinline__ bool wg_item(const PlanDev& P, int wg, int* part_sorted, int* blk) {
-  const int x = wg & 7, k = wg >> 3;
-  const int slot = k / P.tiles;
-  *blk = k - slot * P.tiles;
-  *part_sorted = slot * 8 + x;
-  return *part_sorted < P.total_parts;
-}
-
 struct BWItem {
   const PlanDev* P;
   const uint8_t* q;
@@ -539,8 +531,8 @@ partial_bf16_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   it.g = it.lane >> 4;
   it.l16 = it.lane & 15;
-  int ps, blk;
-  if (!wg_item(P, blockIdx.x, &ps, &blk)) return;
+  int ps, sub, blk;
+  if (!work_item(P, blockIdx.x, &ps, &sub, &blk)) return;
   int e = 0;
   {
     int lo = 0, hi = P.batch - 1;
@@ -560,10 +552,11 @@ partial_bf16_wide_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
   it.ws_stats = ws_stats;
   it.scale_log2 = scale_log2;
   it.b = b;
-  it.part = (int)P.part_base[b] + s;
+  it.part = ((int)P.part_base[b] + s) * P.subs + sub;  // subs > 1: the sub-range slot
   it.L = min(kv_lens[b], (int)P.kv_len[b]);
   it.qb = q_lens != nullptr ? min(max(q_lens[b], 0), P.q_len) : P.q_len;
   split_keys(P, b, s, it.L, kv_bounds, &it.t0, &it.t1);
+  sub_keys(P, sub, &it.t0, &it.t1);
   it.row0 = blk * NT * kTileRows;
   it.p_first = it.t0 / kPage;
   it.p_end = (it.t1 + kPage - 1) / kPage;
@@ -581,7 +574,7 @@ int launch_partial_bf16_wide(const mla_decode_plan_s& plan, const uint8_t* q, co
                              const DeviceArgs* dev, const int32_t* q_lens,
                         const int32_t* kv_bounds) {
   const PlanDev& P = plan.dev;
-  const int slots = (P.total_parts + 7) / 8;
+  const int slots = (P.total_parts * P.subs + 7) / 8;
   const dim3 grid(8 * slots * P.tiles);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   const PlanDev* pd = dev ? dev->plan : nullptr;

@@ -201,17 +201,36 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
     return MLA_ERR_UNSUPPORTED_SHAPE;
   }
   d.total_parts = (int32_t)total;
-  // A split plan that leaves CUs idle with 96-row blocks (a fixed split_kv) takes blocks
-  // of 64 rows instead when the larger grid still fits one wave of the chip: a work
-  // item then costs about two thirds as much, and the extra reads of each page come
-  // from idle CUs' share of HBM. A row's arithmetic does not depend on its block.
-  if (nt == kWideMaxTiles) {
+
+  // Cooperative splits. A grid of at most half as many work items as CUs (a fixed
+  // split_kv over few requests) runs each split on `subs` workgroups, every one over a
+  // run of whole steps of the split's pages, and a fold kernel combines their partial
+  // states into the split's partial: the idle CUs then share the split's key range,
+  // where otherwise each busy CU walks its whole split one step at a time. A run keeps
+  // at least kMinSubSteps steps of the longest split. The partials the pass writes are
+  // still one per (split, row).
+  int64_t max_steps = 0;
+  for (int32_t b = 0; b < batch; ++b) max_steps = std::max(max_steps, ceil_div(chunk_of[b], 2));
+  auto subs_for = [&](int64_t items) {
+    const int64_t by_cus = num_cus / items;
+    const int64_t by_len = max_steps / kMinSubSteps;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_cus, by_len, kMaxSubs}));
+  };
+  // A split plan that leaves CUs idle with 96-row blocks and cannot share its splits
+  // takes blocks of 64 rows instead when the larger grid still fits one wave of the
+  // chip: a work item then costs about two thirds as much, and the extra reads of each
+  // page come from idle CUs' share of HBM. Shared splits are the better use of idle CUs
+  // where they apply (each page still crosses HBM once per 96 rows). A row's arithmetic
+  // does not depend on its block.
+  if (nt == kWideMaxTiles && subs_for(total * tiles) < 2) {
     const int32_t tiles4 = (int32_t)ceil_div(ceil_div(rows, kTileRows), 4);
     if (total <= split_budget(num_cus, tiles4)) {
       d.nt = 4;
       d.tiles = tiles = tiles4;
     }
   }
+  const int32_t subs = subs_for(total * tiles);
+  d.subs = subs;
 
   // Longest request first, so the longest work items start in the first wave.
   std::vector<int32_t> order(batch);
@@ -231,6 +250,10 @@ int build_plan(const int32_t* kv_lens_host, int32_t batch, int32_t q_len, int32_
   plan->num_cus = num_cus;
   plan->ws_o_bytes = align256((size_t)total * rows * kDV * sizeof(float));
   plan->ws_stats_bytes = align256((size_t)total * rows * kStatStride * sizeof(float));
+  if (subs > 1) {
+    plan->ws_sub_o_bytes = align256((size_t)total * subs * rows * kDV * sizeof(float));
+    plan->ws_sub_stats_bytes = align256((size_t)total * subs * rows * kStatStride * sizeof(float));
+  }
   *out = plan;
   return MLA_OK;
 }
@@ -285,6 +308,7 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   d.tiles = tiles;
   d.nt = nt;
   d.total_parts = (int32_t)cap;
+  d.subs = 1;  // the device planner writes whole splits
   plan->device_lengths = 1;
   plan->kv_dtype = kv_dtype;
   plan->max_kv_len = max_kv_len;
@@ -381,7 +405,7 @@ void mla_decode_plan_destroy(mla_decode_plan_t* plan) {
 
 size_t mla_decode_workspace_size(const mla_decode_plan_t* plan) {
   if (plan == nullptr) return 0;
-  return plan->ws_plan_bytes + plan->ws_o_bytes + plan->ws_stats_bytes;
+  return mla::workspace_bytes_of(*plan);
 }
 
 int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,
@@ -395,6 +419,7 @@ int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info
   info->row_tiles = d.tiles;
   info->total_splits = d.total_parts;
   info->work_items = d.total_parts * d.tiles;
+  info->split_workgroups = d.subs;
   info->merge_groups = plan->merge_groups;
   info->merge_slices = plan->merge_slices;
   info->max_splits = plan->max_splits;

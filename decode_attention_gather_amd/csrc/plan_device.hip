@@ -237,6 +237,7 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       // construction; the clamp only keeps a broken bound from reading past them)
       out->total_parts = (int32_t)min(run, (uint32_t)pp.cap_parts);
       out->nt = pp.nt;
+      out->subs = 1;
       // merge width by the host planner's rule, from the actual splits
       int32_t s_max = 0;
       long long s_waves[5] = {0, 0, 0, 0, 0};

@@ -54,7 +54,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("batch", _i32), ("q_len", _i32), ("num_heads", _i32),
                 ("rows_per_request", _i32), ("row_tiles", _i32), ("total_splits", _i32),
                 ("work_items", _i32), ("merge_groups", _i32), ("max_splits", _i32),
-                ("merge_slices", _i32)]
+                ("merge_slices", _i32), ("split_workgroups", _i32)]
 
 
 _lib.mla_decode_plan.restype = ctypes.c_int

@@ -148,6 +148,11 @@ typedef struct {
   int32_t max_splits;       /* max_b S_b */
   int32_t merge_slices;     /* workgroups per row in the merge (1, 2, 4 or 8 slices of
                                the 512 output dims) */
+  int32_t split_workgroups; /* workgroups per (split, row block) in the partial pass: 1,
+                               or up to 8 when the plan has at most half as many work
+                               items as CUs (host plans; each takes a run of whole 64-token
+                               steps of the split, and the pass folds their states into
+                               the split's partial) */
 } mla_decode_plan_info_t;
 
 int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,

@@ -48,9 +48,11 @@ def test_uniform_and_short_plans(lens, q, h, split, exp_splits, exp_chunk):
     info, splits, chunk = p.info()
     assert splits == exp_splits and chunk == exp_chunk
     assert info.rows_per_request == q * h
-    assert info.row_tiles == expected_row_blocks(q * h, sum(splits))
+    steps = max_steps_of(chunk)
+    assert info.row_tiles == expected_row_blocks(q * h, sum(splits), max_steps=steps)
     assert info.total_splits == sum(splits)
     assert info.work_items == sum(splits) * info.row_tiles
+    assert info.split_workgroups == expected_subs(info.work_items, steps)
 
 
 def split_budget(cus, tiles):
@@ -58,11 +60,23 @@ def split_budget(cus, tiles):
     return per_xcd * 8 if per_xcd >= 1 else max(1, cus // tiles)
 
 
-def expected_row_blocks(rows, total_splits=None, cus=256):
+def max_steps_of(chunk_tokens):
+    """2-page steps of the longest split."""
+    return max(math.ceil(c // 32 / 2) for c in chunk_tokens)
+
+
+def expected_subs(items, max_steps, cus=256):
+    """Workgroups per split: as many as idle CUs allow (cus // items), each with at least
+    16 steps of the longest split, at most 8, at least 1."""
+    return max(1, min(cus // items, max_steps // 16, 8))
+
+
+def expected_row_blocks(rows, total_splits=None, cus=256, max_steps=0):
     """Row blocks of 16-row tiles: one block of <= 2 tiles up to 32 rows, otherwise as
     few blocks of <= 6 tiles as cover the rows, each rounded up to 4 or 6 tiles. A plan
-    whose splits leave CUs idle takes blocks of 4 tiles instead of 6 when the larger
-    grid still fits one wave of the chip (total_splits given)."""
+    whose splits leave CUs idle and cannot be shared by several workgroups takes blocks
+    of 4 tiles instead of 6 when the larger grid still fits one wave of the chip
+    (total_splits given)."""
     tiles16 = math.ceil(rows / 16)
     if tiles16 <= 2:
         return 1
@@ -70,7 +84,8 @@ def expected_row_blocks(rows, total_splits=None, cus=256):
     nt = 4 if math.ceil(tiles16 / blocks) <= 4 else 6
     if nt == 6 and total_splits is not None:
         tiles4 = math.ceil(tiles16 / 4)
-        if total_splits <= split_budget(cus, tiles4):
+        shared = expected_subs(total_splits * blocks, max_steps, cus) >= 2
+        if not shared and total_splits <= split_budget(cus, tiles4):
             return tiles4
     return math.ceil(tiles16 / nt)
 
@@ -85,17 +100,37 @@ def test_row_blocks(rows, blocks):
     assert info.row_tiles == blocks
 
 
-@pytest.mark.parametrize("lens,q,h,split,cus,tiles", [
-    ([131072] * 16, 8, 12, 6, 256, 2),   # 96 splits of 96 rows: 192 blocks of 64 rows
-    ([131072] * 16, 8, 12, 0, 256, 1),   # the planner fills the chip with 96-row blocks
-    ([131072] * 16, 8, 12, 6, 128, 1),   # 192 items would not fit 128 CUs
-    ([4096] * 8, 8, 96, 2, 256, 12),     # H96: 16 splits x 12 blocks of 64 rows
-    ([4096] * 8, 8, 96, 4, 256, 8),      # 32 splits x 12 blocks would not fit one wave
+@pytest.mark.parametrize("lens,q,h,split,cus,tiles,subs", [
+    ([131072] * 16, 8, 12, 6, 256, 1, 2),  # 96 splits of 96 rows, two workgroups each
+    ([2048] * 16, 8, 12, 6, 256, 2, 1),    # splits of 6 steps: 192 blocks of 64 rows
+    ([131072] * 16, 8, 12, 0, 256, 1, 1),  # the planner fills the chip with 96-row blocks
+    ([131072] * 16, 8, 12, 6, 128, 1, 1),  # 192 items would not fit 128 CUs
+    ([4096] * 8, 8, 96, 2, 256, 8, 2),     # H96: 16 splits x 8 blocks, shared by two
+    ([1024] * 8, 8, 96, 2, 256, 12, 1),    # short splits: 16 x 12 blocks of 64 rows
+    ([4096] * 8, 8, 96, 4, 256, 8, 1),     # 32 splits x 8 blocks fill the chip
+    ([131072] * 16, 1, 12, 6, 256, 1, 2),  # the headline at split 6: 192 workgroups
+    ([1048576], 1, 12, 100, 256, 1, 2),
+    ([131072], 1, 12, 1, 256, 1, 8),       # at most 8 workgroups per split
+    ([2048], 1, 12, 4, 256, 1, 1),         # splits of 8 steps stay whole
 ])
-def test_underfilled_plans_take_64_row_blocks(lens, q, h, split, cus, tiles):
-    info, splits, _ = plan(lens, q, h, split, cus=cus).info()
-    assert info.row_tiles == tiles == expected_row_blocks(q * h, sum(splits), cus)
+def test_underfilled_plans(lens, q, h, split, cus, tiles, subs):
+    """Idle CUs: splits shared by several workgroups where they are long enough, else
+    64-row blocks for the wide kernel where the larger grid fits one wave."""
+    p = plan(lens, q, h, split, cap=256, cus=cus)
+    info, splits, chunk = p.info()
+    steps = max_steps_of(chunk)
+    assert info.row_tiles == tiles == expected_row_blocks(q * h, sum(splits), cus, steps)
     assert info.work_items == sum(splits) * tiles
+    assert info.split_workgroups == subs == expected_subs(info.work_items, steps, cus)
+    # the workspace holds the split partials and, when shared, one state per workgroup
+    rows = q * h
+    per = (512 + 4) * 4 * rows * sum(splits)
+    assert p.workspace_size() >= per * (1 + (subs if subs > 1 else 0))
+
+
+def test_graph_plans_keep_whole_splits():
+    g = mla.Plan.graph(16, q_len=1, num_heads=12, max_kv_len=131072, split_kv=6, num_cus=256)
+    assert g.info()[0].split_workgroups == 1
 
 
 def check_cover(lens, splits, chunk):
@@ -158,8 +193,14 @@ def test_merge_groups_rule():
 
 
 def test_workspace_size():
-    p = plan([131072] * 16, 8, 12, 6)
+    # 96 splits x 96 rows of fp32 (O, m, l, l~, 0), whole splits (cus 128)
+    p = plan([131072] * 16, 8, 12, 6, cus=128)
+    assert p.info()[0].split_workgroups == 1
     assert p.workspace_size() == 96 * 96 * 512 * 4 + 96 * 96 * 4 * 4
+    # two workgroups per split: their states too
+    p = plan([131072] * 16, 8, 12, 6)
+    assert p.info()[0].split_workgroups == 2
+    assert p.workspace_size() == 3 * (96 * 96 * 512 * 4 + 96 * 96 * 4 * 4)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -374,7 +415,9 @@ def test_bf16_plans_share_the_row_block_rule(rows_q, heads, exp_tiles):
         e = mla.Plan([4096, 100], q_len=rows_q, num_heads=heads, split_kv=2, num_cus=cus)
         info = p.info()[0]
         assert info.row_tiles == e.info()[0].row_tiles
-        assert info.row_tiles == expected_row_blocks(rows_q * heads, info.total_splits, cus)
+        steps = max_steps_of(p.info()[2])
+        assert info.row_tiles == expected_row_blocks(rows_q * heads, info.total_splits, cus,
+                                                     steps)
         assert info.work_items == info.total_splits * info.row_tiles
         if cus == 2:
             assert info.row_tiles == exp_tiles

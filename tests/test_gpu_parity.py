@@ -189,7 +189,7 @@ def test_determinism(mla, heads, q_len):
 
 @pytest.mark.parametrize("lens,split,bounded,dt", [
     ([1, 100, 2049], 3, False, "e4m3"),          # ragged, steps % 3 of 0, 1 and 2
-    ([5000], 1, False, "e4m3"),
+    ([5000], 2, False, "e4m3"),
     ([3 * 32 + 7, 5 * 32, 33], 2, True, "e4m3"),  # key windows inside pages
     ([131072], 6, False, "e4m3"),
     ([1, 100, 2049], 3, False, "bf16"),
@@ -199,17 +199,22 @@ def test_loader_depth_same_bits(mla, lens, split, bounded, dt):
     """The one-tile kernels run another schedule when the grid has fewer work items than
     CUs (E4M3: three steps of loads in flight per loader instead of two; both: the
     waves' roles placed so that the QK SIMDs carry loaders): the partials (workspace)
-    must be the same bits either way. num_cus 1 makes every grid full."""
+    must be the same bits either way. num_cus 1 makes every grid full; 2 items - 1 CUs
+    leaves the grid under-filled while every split still runs on one workgroup."""
     case = inputs.make_case(lens, num_heads=12, q_len=1, seed=41, split_kv=split, kv_dtype=dt)
     dc = mla.to_device(case)
     kvb = None
     if bounded:
         kvb = torch.tensor([[min(5, n), n] for n in lens], dtype=torch.int32, device="cuda")
     _say(f"[gpu] under-filled schedule lens={lens} split={split} bounded={bounded} {dt}")
+    items = mla.Plan(dc.kv_lens_host, q_len=1, num_heads=12, split_kv=split, num_cus=1,
+                     kv_dtype=dt).info()[0].work_items
+    assert items >= 2
     ws = []
-    for cus in (256, 1):
+    for cus in (2 * items - 1, 1):
         plan = mla.Plan(dc.kv_lens_host, q_len=1, num_heads=12, split_kv=split, num_cus=cus,
                         kv_dtype=dt)
+        assert plan.info()[0].split_workgroups == 1
         w = torch.zeros(plan.workspace_size(), dtype=torch.uint8, device="cuda")
         mla.partial_ex(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, case.softmax_scale, w,
                        kv_bounds=kvb)
