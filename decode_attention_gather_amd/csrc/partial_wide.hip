@@ -5,8 +5,8 @@
 // "trtllm-gen FMHA: split the KV partials of a row across thread groups in
 // fmhaReductionKernel" (Description: per-row max, sum and unnormalised O) over the
 // split's keys, with the causal limit of the MTP verify shape (issue #20510 "CuTe DSL
-// FP8 MLA decode slower after #19338", Setup). P~ is the two-term E4M3 form of the BF16
-// rounding of x = 2^(t - c + 8) (the QK waves hand x to the PV waves as BF16); it
+// FP8 MLA decode slower after #19338", Setup). P~ is the two-term E4M3 form of the FP16
+// rounding of x = 2^(t - c + 8) (the QK waves hand x to the PV waves as FP16); it
 // depends only on the page's own scores, so the partials are the same under every
 // split plan.
 //
@@ -27,9 +27,10 @@
 //    computes S^T = K Q^T for both pages of the step: the 512 latent bytes on
 //    v_mfma_scale_f32_16x16x128_f8f6f4, the 64 rope bytes on two
 //    v_mfma_f32_16x16x32_fp8_fp8; every K fragment read from LDS feeds NT/2 MFMAs. Softmax as in the narrow kernel:
-//    per (row, page) c = ceil(max t), x = 2^(t - c + 8), written to LDS as BF16; the
-//    PV waves split it into P~ = hi + lo / 16 (hi = e4m3(x), lo = e4m3(16 (x - hi))),
-//    which moves most of the quantisation work off the QK waves.
+//    per (row, page) c = ceil(max t), x = 2^(t - c + 8), written to LDS as FP16; the
+//    PV waves split it into P~ = hi + lo / 16 (hi = e4m3(x), lo = e4m3(16 (x - hi)))
+//    with the packed FP16 conversions of gfx950 (x - hi is exact in FP16), which keeps
+//    the quantisation work off the QK waves.
 //    The QK waves also keep each row's running maximum m (an integer) and l = sum x,
 //    and publish per step the rescale factor 2^(m_old - m_new) and the page exponents
 //    c_page - m_new; l~ = sum P~ comes from one PV MFMA against a tile of ones.
@@ -54,7 +55,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kStepPages = 2;
@@ -64,7 +66,7 @@ constexpr int kChunks = kDQK / 16;                   // 36 chunks of 16 bytes pe
 constexpr int kStepLoads = kStepBytes / 1024;        // 36 wave-wide 16-byte loads per step
 constexpr int kPageLoads = kPageBytes / 1024;        // 18 of them per page
 static_assert(kStepLoads * 1024 == kStepBytes && kPageBytes % 1024 == 0, "1 KB loads tile a step");
-constexpr int kPRow = 144;                           // row of x: 64 BF16 + 16 bytes of pad
+constexpr int kPRow = 144;                           // row of x: 64 FP16 + 16 bytes of pad
 constexpr int kOnesE4M3 = 0x38383838;                // four E4M3 1.0
 
 // Roles (at most 2 waves per SIMD, so every wave may hold 256 VGPRs):
@@ -312,7 +314,7 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
         float sx = 0.f;
         const int row = (qw * kT + k) * kTileRows + l16;
         // page token 16 tt + 4 g + jj goes to K position 32 p + 16 (g >> 1) + 8 tt + 4 (g & 1) + jj;
-        // the QK wave hands x over as BF16 (2 bytes per position), the PV waves split it
+        // the QK wave hands x over as FP16 (2 bytes per position), the PV waves split it
         uint8_t* prow = sm.ptile[st & 1] + row * kPRow + 2 * (32 * p + 16 * (g >> 1) + 4 * (g & 1));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -322,8 +324,8 @@ __device__ __forceinline__ void wide_qk(const WItem& it, WSmem<NT>& sm) {
             x[jj] = __builtin_amdgcn_exp2f(t[tt][jj] + off);  // v_exp_f32; exp2(-inf) = 0
             sx += x[jj];
           }
-          *(v2bf*)(prow + 16 * tt) = v2bf{(__bf16)x[0], (__bf16)x[1]};
-          *(v2bf*)(prow + 16 * tt + 4) = v2bf{(__bf16)x[2], (__bf16)x[3]};
+          *(v2h*)(prow + 16 * tt) = v2h{(_Float16)x[0], (_Float16)x[1]};
+          *(v2h*)(prow + 16 * tt + 4) = v2h{(_Float16)x[2], (_Float16)x[3]};
         }
         cpg[k][p] = c;
         xs[k][p] = sx;
@@ -502,28 +504,26 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
       const float2 e = sm.sc[pb][rt * kTileRows + l16];
       const float ep = (g & 1) ? e.y : e.x;
       sa[k] = ep == -INFINITY ? 127 : max(0, 127 + (int)ep - 4 * (g >> 1));
-      // P~ of K positions 16 g .. 16 g + 15 from the BF16 x the QK wave left:
-      // hi = e4m3(x), lo = e4m3(16 (x - hi)), both exact functions of that BF16 value
+      // P~ of K positions 16 g .. 16 g + 15 from the FP16 x the QK wave left:
+      // hi = e4m3(x), lo = e4m3(16 (x - hi)); x - hi is exact in FP16, and the scaled
+      // conversion divides by its scale (1/16 gives the factor 16)
       const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 32 * g;
       const v4i xa = ld16(prow, 0), xb = ld16(prow, 16);
       const int xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
       int hw[4], lw[4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
-        const float x0 = __uint_as_float((uint32_t)xw[2 * w4] << 16);
-        const float x1 = __uint_as_float((uint32_t)xw[2 * w4] & 0xFFFF0000u);
-        const float x2 = __uint_as_float((uint32_t)xw[2 * w4 + 1] << 16);
-        const float x3 = __uint_as_float((uint32_t)xw[2 * w4 + 1] & 0xFFFF0000u);
-        int h = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-        h = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, h, true);
-        const float h0 = __builtin_amdgcn_cvt_f32_fp8(h, 0);
-        const float h1 = __builtin_amdgcn_cvt_f32_fp8(h, 1);
-        const float h2 = __builtin_amdgcn_cvt_f32_fp8(h, 2);
-        const float h3 = __builtin_amdgcn_cvt_f32_fp8(h, 3);
-        int l = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - h0) * 16.f, (x1 - h1) * 16.f, 0, false);
-        l = __builtin_amdgcn_cvt_pk_fp8_f32((x2 - h2) * 16.f, (x3 - h3) * 16.f, l, true);
-        hw[w4] = h;
-        lw[w4] = l;
+        const v2h x01 = __builtin_bit_cast(v2h, xw[2 * w4]);
+        const v2h x23 = __builtin_bit_cast(v2h, xw[2 * w4 + 1]);
+        v2s h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v2s{0, 0}, x01, 1.0f, false);
+        h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(h, x23, 1.0f, true);
+        const int hi = __builtin_bit_cast(int, h);
+        const v2h d01 = x01 - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+        const v2h d23 = x23 - __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+        v2s l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v2s{0, 0}, d01, 0.0625f, false);
+        l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(l, d23, 0.0625f, true);
+        hw[w4] = hi;
+        lw[w4] = __builtin_bit_cast(int, l);
       }
       pa[k] = v8i{hw[0], hw[1], hw[2], hw[3], lw[0], lw[1], lw[2], lw[3]};
       if (k == dh) {
