@@ -482,34 +482,58 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
   // step st + 2 (when dma) issued together after the first dim tile's MFMAs
   auto pv_step = [&](int st, bool dma, uint64_t gp) {
     const int pb = st & 1;
+    const uint32_t sb = stage_of(st), dst = stage_of(st + 2);
+    const uint32_t v0 = sb + tr_base[0], v1 = sb + tr_base[1];
+    // LDS reads of the step's small operands first (per row tile: the rescale factors of
+    // result rows rt 16 + 4 g + jj, the page exponents of operand row rt 16 + l16 and
+    // its 16 x values), then the first dim tiles' V, so that the P~ split's VALU work
+    // covers the V reads' latency and no wait for the small reads also waits for V
+    float4 al[kRT];
+    float ep[kRT];  // page exponent of K block g = (term g >> 1, page g & 1)
+    v4i xa[kRT], xb[kRT];
+#pragma unroll
+    for (int k = 0; k < kRT; ++k) {
+      const int rt = rt0 + k;
+      al[k] = *(const float4*)&sm.alpha[pb][rt * kTileRows + 4 * g];
+      const float2 e = sm.sc[pb][rt * kTileRows + l16];
+      const float ex = e.x, ey = e.y;
+      ep[k] = (g & 1) ? ey : ex;
+      const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 32 * g;
+      xa[k] = ld16(prow, 0);
+      xb[k] = ld16(prow, 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kPre = 2;
+    v2i pre0[kPre], pre1[kPre];
+#pragma unroll
+    for (int d = 0; d < kPre; ++d) {
+      pre0[d] = lds_tr8(v0 + 16 * d);
+      pre1[d] = lds_tr8(v1 + 16 * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     int sa[kRT];
     v8i pa[kRT];
 #pragma unroll
     for (int k = 0; k < kRT; ++k) {
-      const int rt = rt0 + k;
-      // result rows rt 16 + 4 g + jj: rescale when the running max moved
-      const float4 al = *(const float4*)&sm.alpha[pb][rt * kTileRows + 4 * g];
-      const bool rescale = al.x != 1.f || al.y != 1.f || al.z != 1.f || al.w != 1.f;
+      // rescale when the running max moved
+      const float4 a4 = al[k];
+      const bool rescale = a4.x != 1.f || a4.y != 1.f || a4.z != 1.f || a4.w != 1.f;
       if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
         for (int d = 0; d < kDT; ++d) {
-          acc[k][d][0] *= al.x; acc[k][d][1] *= al.y;
-          acc[k][d][2] *= al.z; acc[k][d][3] *= al.w;
+          acc[k][d][0] *= a4.x; acc[k][d][1] *= a4.y;
+          acc[k][d][2] *= a4.z; acc[k][d][3] *= a4.w;
         }
         if (k == dh) {
-          acc1[0] *= al.x; acc1[1] *= al.y; acc1[2] *= al.z; acc1[3] *= al.w;
+          acc1[0] *= a4.x; acc1[1] *= a4.y; acc1[2] *= a4.z; acc1[3] *= a4.w;
         }
       }
-      // operand row rt 16 + l16: E8M0 scale of K block g = (term g >> 1, page g & 1)
-      const float2 e = sm.sc[pb][rt * kTileRows + l16];
-      const float ep = (g & 1) ? e.y : e.x;
-      sa[k] = ep == -INFINITY ? 127 : max(0, 127 + (int)ep - 4 * (g >> 1));
+      // E8M0 scale of K block g
+      sa[k] = ep[k] == -INFINITY ? 127 : max(0, 127 + (int)ep[k] - 4 * (g >> 1));
       // P~ of K positions 16 g .. 16 g + 15 from the FP16 x the QK wave left:
       // hi = e4m3(x), lo = e4m3(16 (x - hi)); x - hi is exact in FP16, and the scaled
       // conversion divides by its scale (1/16 gives the factor 16)
-      const uint8_t* prow = sm.ptile[pb] + (rt * kTileRows + l16) * kPRow + 32 * g;
-      const v4i xa = ld16(prow, 0), xb = ld16(prow, 16);
-      const int xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const int xw[8] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w, xb[k].x, xb[k].y, xb[k].z, xb[k].w};
       int hw[4], lw[4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
@@ -534,12 +558,10 @@ __device__ __forceinline__ void wide_pv(const WItem& it, WSmem<NT>& sm) {
     }
     // V: byte j of word w of the operand is step token 32 (g >> 1) + 16 (w >> 1) +
     // 8 (g & 1) + 4 (w & 1) + j; rows past the split's end were zeroed in LDS
-    const uint32_t sb = stage_of(st), dst = stage_of(st + 2);
-    const uint32_t v0 = sb + tr_base[0], v1 = sb + tr_base[1];
 #pragma unroll
     for (int d = 0; d < kDT; ++d) {
-      const v2i b0 = lds_tr8(v0 + 16 * d);
-      const v2i b1 = lds_tr8(v1 + 16 * d);
+      const v2i b0 = d < kPre ? pre0[d < kPre ? d : 0] : lds_tr8(v0 + 16 * d);
+      const v2i b1 = d < kPre ? pre1[d < kPre ? d : 0] : lds_tr8(v1 + 16 * d);
       const v8i vb = v8i{b0.x, b0.y, b1.x, b1.y, b0.x, b0.y, b1.x, b1.y};
 #pragma unroll
       for (int k = 0; k < kRT; ++k)
