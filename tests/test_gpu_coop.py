@@ -133,3 +133,44 @@ def test_cooperative_splits(mla, lens, heads, q_len, split, dt, bounded, ragged)
         err = np.abs(oa[r] - o_ref[i])
         assert (err <= 1e-2 + 1e-2 * np.abs(o_ref[i])).all(), (r, float(err.max()))
         assert abs(la[r] - lse_ref[i]) <= 1e-4 * max(1.0, abs(lse_ref[i])), r
+
+
+def test_cooperative_splits_in_a_hip_graph(mla):
+    """A host plan with shared splits enqueues three kernels (partial, fold, merge) and no
+    memset, so a captured call replays: every replay, with the cache changed in between,
+    equals the eager call on the same inputs."""
+    case = inputs.make_case([20000, 3000], num_heads=12, q_len=1, seed=53, split_kv=2)
+    dc = mla.to_device(case)
+    plan = mla.Plan(dc.kv_lens_host, q_len=1, num_heads=12, split_kv=2, num_cus=256)
+    assert plan.info()[0].split_workgroups > 1
+    ws = plan.alloc_workspace()
+    rows = 2 * 12
+    o = torch.empty((rows, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+               dc.output_scale, ws, o, lse)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+                   dc.output_scale, ws, o, lse, stream=s)
+    torch.cuda.synchronize()
+    q0 = dc.q.clone()
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for i in range(4):
+        _say(f"[gpu] shared splits in a HIP graph: replay {i}")
+        if i:  # new queries (the heads' rows permuted) between replays
+            perm = torch.randperm(12, generator=gen).to("cuda")
+            dc.q.copy_(q0.view(2, 1, 12, -1)[:, :, perm].reshape(q0.shape))
+            torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, lse_g = o.clone(), lse.clone()
+        o_e = torch.empty_like(o)
+        lse_e = torch.empty_like(lse)
+        mla.decode(plan, dc.q, dc.kv, dc.block_table, dc.kv_lens, dc.softmax_scale,
+                   dc.output_scale, plan.alloc_workspace(), o_e, lse_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(lse_g, lse_e), f"replay {i}"

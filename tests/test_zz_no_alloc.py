@@ -33,7 +33,8 @@ def _both(mla, case, split):
 @pytest.mark.parametrize("first,second", [
     (([131072] * 4, 12, 1, 0), ([700, 33], 12, 2, 3)),        # narrow kernel, then smaller
     (([4096, 20000], 12, 8, 0), ([3000], 12, 8, 4)),           # wide kernel, then smaller
-], ids=["narrow", "wide"])
+    (([131072] * 2, 12, 1, 2), ([20000], 12, 1, 1)),           # shared splits (and the fold)
+], ids=["narrow", "wide", "shared"])
 def test_noalloc_matches_decode(mla, first, second):
     for i, (lens, heads, q_len, split) in enumerate((first, second)):
         print(f"[gpu] noalloc call {i}: lens={lens} H={heads} q={q_len} split={split}",
