@@ -12,7 +12,8 @@
 // shape applies (issue #20510 "CuTe DSL FP8 MLA decode slower after #19338", Setup).
 //
 // Design for gfx950: one workgroup per work item (10 wavefronts for one row tile, 16 for
-// two), one work item per CU.
+// two), one work item per CU; on plans that would leave CUs idle a work item is a run of
+// whole steps of a split, and a fold kernel combines the runs' states.
 //  * Page gather, register-staged: loader waves read the split's pages with 16-byte
 //    global loads into VGPRs two steps (2 pages each) ahead of use and store them into
 //    a 3-stage LDS ring. A page is one contiguous 18 KB block of HBM, so every load

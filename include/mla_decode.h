@@ -132,8 +132,10 @@ void mla_decode_plan_destroy(mla_decode_plan_t* plan);
 int mla_decode_plan_with_merge_bound(const mla_decode_plan_t* plan, int32_t max_groups,
                                      mla_decode_plan_t** out);
 
-/* Bytes of workspace the plan needs (fp32 partials: (512 + 4) * 4 bytes per
- * (row, split)). 0 for a NULL plan. */
+/* Bytes of workspace the plan needs: fp32 partials, (512 + 4) * 4 bytes per (row,
+ * split), and with split_workgroups > 1 (mla_decode_plan_get_info) as much again per
+ * workgroup of a split for their states before the fold; graph plans also keep their
+ * device plan at its head. 0 for a NULL plan. */
 size_t mla_decode_workspace_size(const mla_decode_plan_t* plan);
 
 /* Introspection, for tests and logs. splits/chunk_tokens may be NULL; otherwise they
@@ -163,7 +165,10 @@ int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info
  * for every (request, split, row block) it gathers the split's pages into LDS with
  * 16-byte loads, forms QK^T on FP8 MFMA with fp32 accumulation, runs an exp2 online
  * softmax, and forms PV on FP8 MFMA with V read from the same LDS rows, writing fp32
- * partials to the workspace. softmax_scale is the fp32 scale on q . k.
+ * partials to the workspace. softmax_scale is the fp32 scale on q . k. A host plan whose
+ * splits would leave CUs idle (split_workgroups > 1) runs each split on several
+ * workgroups and folds their states in a second kernel; either way the workspace ends
+ * with one partial per (split, row).
  */
 int mla_decode_partial(const mla_decode_plan_t* plan, const void* q, const void* kv_cache,
                        const int32_t* block_table, int64_t bt_stride,
