@@ -252,11 +252,12 @@ merge_kernel(const PlanDev Parg, const PlanDev* __restrict__ pdev,
 //     M = max_i m_i,  O = sum_i 2^(m_i - M) O_i,  l = sum_i 2^(m_i - M) l_i  (same for l~),
 // in sub-range order. One wavefront per (split, row); lane i owns dims [8 i, 8 i + 8).
 __global__ void __launch_bounds__(256)
-fold_kernel(int n, int rows, int subs, const float* __restrict__ sub_o,
-            const float* __restrict__ sub_stats, float* __restrict__ o,
-            float* __restrict__ stats) {
+fold_kernel(int n, int rows, int subs, const PlanDev* __restrict__ pdev,
+            const float* __restrict__ sub_o, const float* __restrict__ sub_stats,
+            float* __restrict__ o, float* __restrict__ stats) {
   const int w = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-  if (w >= n) return;
+  // graph plans: the launch covers the capacity, the device plan the splits that exist
+  if (w >= n || (pdev != nullptr && w >= pdev->total_parts * rows)) return;
   const int lane = threadIdx.x & 63;
   const int p = w / rows, r = w - p * rows;
   const int64_t k0 = (int64_t)p * subs * rows + r;  // slot of (p, sub 0, r); sub i: + i rows
@@ -286,12 +287,12 @@ fold_kernel(int n, int rows, int subs, const float* __restrict__ sub_o,
 }  // namespace
 
 int launch_fold(const mla_decode_plan_s& plan, const float* sub_o, const float* sub_stats,
-                float* o, float* stats, void* stream) {
+                float* o, float* stats, void* stream, const DeviceArgs* dev) {
   const PlanDev& P = plan.dev;
-  const int n = P.total_parts * P.rows;
+  const int n = P.total_parts * P.rows;  // graph plans: the capacity
   if (n == 0) return 0;
   hipLaunchKernelGGL(fold_kernel, dim3((n + 3) / 4), dim3(256), 0, (hipStream_t)stream, n,
-                     P.rows, P.subs, sub_o, sub_stats, o, stats);
+                     P.rows, P.subs, dev ? dev->plan : nullptr, sub_o, sub_stats, o, stats);
   return (int)hipGetLastError();
 }
 

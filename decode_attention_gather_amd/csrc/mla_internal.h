@@ -27,7 +27,7 @@ constexpr int kStatStride = 4;             // (m, l, l~, 0) per (split, row)
 constexpr int kMergeWavesPerCu = 32;      // merge launch budget: waves resident per CU
 constexpr int kMaxMergeSlices = 8;         // merge: at most 8 workgroups per row
 constexpr int kMaxSubs = 8;                // workgroups sharing one split (small grids)
-constexpr int kMinSubSteps = 16;           // 2-page steps per workgroup when shared
+constexpr int kMinSubSteps = 2;            // 2-page steps per workgroup when shared
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroup i runs on XCD i mod 8
 
 // Everything the kernels need from a plan, passed by value as a kernel argument
@@ -197,7 +197,7 @@ int launch_merge(const mla_decode_plan_s& plan, const float* ws_o, const float* 
 // Split partials from their sub-ranges' partial states (dev.subs > 1): reads sub_o /
 // sub_stats ([split][sub][row]), writes o / stats ([split][row]).
 int launch_fold(const mla_decode_plan_s& plan, const float* sub_o, const float* sub_stats,
-                float* o, float* stats, void* stream);
+                float* o, float* stats, void* stream, const DeviceArgs* dev = nullptr);
 // Splits that fill the chip once for row blocks of `tiles` (XCD-aware; plan.cpp).
 int64_t split_budget(int32_t num_cus, int32_t tiles);
 int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, PlanDev* out,

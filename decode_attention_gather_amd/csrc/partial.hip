@@ -601,7 +601,7 @@ int launch_partial(const mla_decode_plan_s& plan, const uint8_t* q, const uint8_
   const int rc = launch_partial_kernel(plan, q, kv, bt, bt_stride, kv_lens, softmax_scale,
                                        sub_o, sub_stats, stream, dev, q_lens, kv_bounds);
   if (rc != 0) return rc;
-  return launch_fold(plan, sub_o, sub_stats, ws_o, ws_stats, stream);
+  return launch_fold(plan, sub_o, sub_stats, ws_o, ws_stats, stream, dev);
 }
 
 }  // namespace mla

@@ -308,7 +308,16 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   d.tiles = tiles;
   d.nt = nt;
   d.total_parts = (int32_t)cap;
-  d.subs = 1;  // the device planner writes whole splits
+  // Shared splits as in host plans, decided here from the capacity and the length bound
+  // (uniform split_kv only: the proportional planner fills the chip); the device planner
+  // copies the count into every device plan.
+  d.subs = 1;
+  if (split_kv > 0) {
+    const int64_t longest = ceil_div(max_pages, std::min<int64_t>(per_req, max_pages));
+    const int64_t by_cus = num_cus / (cap * tiles);
+    const int64_t by_len = ceil_div(longest, 2) / kMinSubSteps;
+    d.subs = (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_cus, by_len, kMaxSubs}));
+  }
   plan->device_lengths = 1;
   plan->kv_dtype = kv_dtype;
   plan->max_kv_len = max_kv_len;
@@ -334,6 +343,11 @@ int build_graph_plan(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   plan->ws_plan_bytes = align256(sizeof(PlanDev));
   plan->ws_o_bytes = align256((size_t)cap * rows * kDV * sizeof(float));
   plan->ws_stats_bytes = align256((size_t)cap * rows * kStatStride * sizeof(float));
+  if (d.subs > 1) {
+    plan->ws_sub_o_bytes = align256((size_t)cap * d.subs * rows * kDV * sizeof(float));
+    plan->ws_sub_stats_bytes =
+        align256((size_t)cap * d.subs * rows * kStatStride * sizeof(float));
+  }
   *out = plan;
   return MLA_OK;
 }

@@ -77,6 +77,7 @@ struct PlanParams {
   int32_t batch, q_len, heads, rows, tiles, nt;
   int32_t max_kv_len, split_kv, max_split_kv, num_cus, cap_parts, max_groups;
   int32_t budget;  // splits that fill the chip once
+  int32_t subs;    // workgroups per (split, row block), decided by the host
 };
 
 __global__ void __launch_bounds__(kPlanThreads)
@@ -237,7 +238,7 @@ device_plan_kernel(const PlanParams pp, const int32_t* __restrict__ kv_lens,
       // construction; the clamp only keeps a broken bound from reading past them)
       out->total_parts = (int32_t)min(run, (uint32_t)pp.cap_parts);
       out->nt = pp.nt;
-      out->subs = 1;
+      out->subs = pp.subs;
       // merge width by the host planner's rule, from the actual splits
       int32_t s_max = 0;
       long long s_waves[5] = {0, 0, 0, 0, 0};
@@ -275,6 +276,7 @@ int launch_device_plan(const mla_decode_plan_s& plan, const int32_t* kv_lens, Pl
   pp.cap_parts = d.total_parts;
   pp.max_groups = plan.merge_groups;
   pp.budget = (int32_t)split_budget(plan.num_cus, d.tiles);
+  pp.subs = d.subs;
   hipLaunchKernelGGL(device_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
                      pp, kv_lens, out);
   return (int)hipGetLastError();

@@ -152,9 +152,10 @@ typedef struct {
                                the 512 output dims) */
   int32_t split_workgroups; /* workgroups per (split, row block) in the partial pass: 1,
                                or up to 8 when the plan has at most half as many work
-                               items as CUs (host plans; each takes a run of whole 64-token
+                               items as CUs (host plans, and graph plans with a uniform
+                               split_kv, by capacity); each takes a run of whole 64-token
                                steps of the split, and the pass folds their states into
-                               the split's partial) */
+                               the split's partial */
 } mla_decode_plan_info_t;
 
 int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info_t* info,
@@ -165,7 +166,7 @@ int mla_decode_plan_get_info(const mla_decode_plan_t* plan, mla_decode_plan_info
  * for every (request, split, row block) it gathers the split's pages into LDS with
  * 16-byte loads, forms QK^T on FP8 MFMA with fp32 accumulation, runs an exp2 online
  * softmax, and forms PV on FP8 MFMA with V read from the same LDS rows, writing fp32
- * partials to the workspace. softmax_scale is the fp32 scale on q . k. A host plan whose
+ * partials to the workspace. softmax_scale is the fp32 scale on q . k. A plan whose
  * splits would leave CUs idle (split_workgroups > 1) runs each split on several
  * workgroups and folds their states in a second kernel; either way the workspace ends
  * with one partial per (split, row).

@@ -67,8 +67,8 @@ def max_steps_of(chunk_tokens):
 
 def expected_subs(items, max_steps, cus=256):
     """Workgroups per split: as many as idle CUs allow (cus // items), each with at least
-    16 steps of the longest split, at most 8, at least 1."""
-    return max(1, min(cus // items, max_steps // 16, 8))
+    2 steps of the longest split, at most 8, at least 1."""
+    return max(1, min(cus // items, max_steps // 2, 8))
 
 
 def expected_row_blocks(rows, total_splits=None, cus=256, max_steps=0):
@@ -102,16 +102,17 @@ def test_row_blocks(rows, blocks):
 
 @pytest.mark.parametrize("lens,q,h,split,cus,tiles,subs", [
     ([131072] * 16, 8, 12, 6, 256, 1, 2),  # 96 splits of 96 rows, two workgroups each
-    ([2048] * 16, 8, 12, 6, 256, 2, 1),    # splits of 6 steps: 192 blocks of 64 rows
+    ([512] * 16, 8, 12, 6, 256, 2, 1),     # splits of 2 steps: 192 blocks of 64 rows
     ([131072] * 16, 8, 12, 0, 256, 1, 1),  # the planner fills the chip with 96-row blocks
     ([131072] * 16, 8, 12, 6, 128, 1, 1),  # 192 items would not fit 128 CUs
     ([4096] * 8, 8, 96, 2, 256, 8, 2),     # H96: 16 splits x 8 blocks, shared by two
-    ([1024] * 8, 8, 96, 2, 256, 12, 1),    # short splits: 16 x 12 blocks of 64 rows
+    ([256] * 8, 8, 96, 2, 256, 12, 1),     # short splits: 16 x 12 blocks of 64 rows
     ([4096] * 8, 8, 96, 4, 256, 8, 1),     # 32 splits x 8 blocks fill the chip
     ([131072] * 16, 1, 12, 6, 256, 1, 2),  # the headline at split 6: 192 workgroups
     ([1048576], 1, 12, 100, 256, 1, 2),
     ([131072], 1, 12, 1, 256, 1, 8),       # at most 8 workgroups per split
-    ([2048], 1, 12, 4, 256, 1, 1),         # splits of 8 steps stay whole
+    ([2048], 1, 12, 4, 256, 1, 4),         # splits of 8 steps: 4 runs of 2 steps
+    ([96], 1, 12, 3, 256, 1, 1),           # one-step splits stay whole
 ])
 def test_underfilled_plans(lens, q, h, split, cus, tiles, subs):
     """Idle CUs: splits shared by several workgroups where they are long enough, else
@@ -128,8 +129,16 @@ def test_underfilled_plans(lens, q, h, split, cus, tiles, subs):
     assert p.workspace_size() >= per * (1 + (subs if subs > 1 else 0))
 
 
-def test_graph_plans_keep_whole_splits():
+def test_graph_plans_share_uniform_splits():
+    """Graph plans decide shared splits on the host from the capacity and the length
+    bound (uniform split_kv only); here they match the host plan of those lengths."""
+    for B, L, split in ((16, 131072, 6), (2, 40000, 2), (1, 1 << 20, 100), (2, 3000, 4)):
+        g = mla.Plan.graph(B, q_len=1, num_heads=12, max_kv_len=L, split_kv=split, num_cus=256)
+        h = plan([L] * B, 1, 12, split, cap=256)
+        assert g.info()[0].split_workgroups == h.info()[0].split_workgroups
     g = mla.Plan.graph(16, q_len=1, num_heads=12, max_kv_len=131072, split_kv=6, num_cus=256)
+    assert g.info()[0].split_workgroups == 2
+    g = mla.Plan.graph(16, q_len=1, num_heads=12, max_kv_len=131072, split_kv=0, num_cus=256)
     assert g.info()[0].split_workgroups == 1
 
 
@@ -285,7 +294,13 @@ def test_graph_plan_capacity(batch, max_len, q, h, split, cap_parts):
     head = 3840  # the device plan (PlanDev, 3616 bytes) at the workspace head, 256-aligned
     o = (cap_parts * rows * 2048 + 255) // 256 * 256
     st = (cap_parts * rows * 16 + 255) // 256 * 256
-    assert p.workspace_size() == head + o + st
+    subs = info.split_workgroups  # shared splits keep one state per workgroup too
+    assert (subs > 1) == (split > 0 and cap_parts * info.row_tiles * 2 <= 256)
+    extra = 0
+    if subs > 1:
+        extra = ((cap_parts * subs * rows * 2048 + 255) // 256 * 256
+                 + (cap_parts * subs * rows * 16 + 255) // 256 * 256)
+    assert p.workspace_size() == head + o + st + extra
 
 
 def test_graph_plan_capacity_covers_device_plans():

@@ -47,6 +47,9 @@ GRAPH_CASES = [
     ("q8_planner", [4096, 700, 65], None, 12, 8, 0),
     ("h96_q1", [2000, 300], None, 96, 1, 0),
     ("q2_h16", [1500, 40, 2], None, 16, 2, 0),
+    ("shared_uniform", [40000, 30000], None, 12, 1, 2),         # 8 workgroups per split
+    ("shared_shorter", [40000, 40000], [39000, 5000], 12, 1, 2),
+    ("shared_q8", [20000, 9000], None, 12, 8, 1),
 ]
 
 
@@ -103,12 +106,15 @@ def test_graph_zero_length_request(mla):
     assert_parity(o[12:], lse[12:], o_ref, lse_ref, "zero-length neighbour")
 
 
-def test_graph_capture_replay(mla):
-    """One captured call, replayed while the device lengths and scales change."""
+@pytest.mark.parametrize("split", [0, 2], ids=["planner", "uniform_shared"])
+def test_graph_capture_replay(mla, split):
+    """One captured call, replayed while the device lengths and scales change (with a
+    uniform split_kv of 2 each split is shared by several workgroups and folded)."""
     # the cache holds 6000 valid tokens for every request; the device lengths vary below
-    case = inputs.make_case([6000] * 4, num_heads=12, q_len=2, seed=99, split_kv=0)
+    case = inputs.make_case([6000] * 4, num_heads=12, q_len=2, seed=99, split_kv=split)
     dc = mla.to_device(case)
-    plan = mla.Plan.graph(4, q_len=2, num_heads=12, max_kv_len=6000)
+    plan = mla.Plan.graph(4, q_len=2, num_heads=12, max_kv_len=6000, split_kv=split)
+    assert (plan.info()[0].split_workgroups > 1) == (split > 0)
     ws = plan.alloc_workspace()
     lens = [6000, 900, 33, 2500]
     lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
